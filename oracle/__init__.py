@@ -1,0 +1,34 @@
+"""CPU oracle for permuted, early-stopping block-sparse causal prefill attention.
+
+TEST INFRASTRUCTURE. This package is the slow, plain reference that the GPU
+path is checked against. Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import it. The product package
+(``permuted_block_sparse_amd``) never imports it, and it imports nothing from
+the product: the two share no kernels, helpers, constants or tables. Its only
+inputs are bfloat16 bit patterns (``uint16`` arrays) produced by the seeded
+generator in ``synthetic/``.
+
+Arithmetic: int64 for every ranking score (exact), float64 for everything
+real, computed from the exact values of the bfloat16 inputs.
+
+Pinned parts (see tests/test_oracle_*.py):
+  * dense causal attention (Eq. (1) of the AB-Sparse page) -- against torch's
+    float64 scaled-dot-product attention, closed forms and causality;
+  * the S2O steps -- tau = 0 reproduces dense attention for every flag
+    combination and for any key/value order; one segment reproduces dense
+    attention for any tau; a closed form for the stop point with constant
+    keys; brute-force restricted attention on tiny inputs; brute-force
+    ranking of the two orders; worked examples of both orders; a golden
+    fixture in tests/golden/.
+Parity unpinned: the agreement of the sparsity/MSE figures with the numbers
+printed on the S2O summary page (those need real models and datasets).
+"""
+from .s2o import (SA_NO_QPERM, SA_NO_KVPERM, SA_NO_EARLYSTOP, Plan,
+                  decode_bf16, fixed_point, dense_causal, plan, stop_points,
+                  attend, s2o_attention, selected_counts, metrics,
+                  restricted_list, kappa_of)
+
+__all__ = ["SA_NO_QPERM", "SA_NO_KVPERM", "SA_NO_EARLYSTOP", "Plan",
+           "decode_bf16", "fixed_point", "dense_causal", "plan",
+           "stop_points", "attend", "s2o_attention", "selected_counts",
+           "metrics", "restricted_list", "kappa_of"]

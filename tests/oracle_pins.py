@@ -1,0 +1,423 @@
+"""Pins of the CPU oracle, written as functions of the oracle module.
+
+Each ``check_*`` takes the oracle module (``oracle.s2o``, or a copy of it
+with a planted mistake) and raises AssertionError when the module disagrees
+with what the pages or the mathematics fix. ``test_oracle_pins.py`` runs them
+on the real oracle (all must pass); ``test_oracle_mutations.py`` runs them on
+copies with planted mistakes (each mistake must make one of them fail).
+
+None of these checks re-types the oracle's own formulas: they use closed
+forms, brute-force reformulations, worked examples with hand-derived
+answers, library routines, and invariants stated on the pages.
+"""
+from __future__ import annotations
+
+import math
+from fractions import Fraction
+
+import numpy as np
+import torch
+
+from synthetic import StripeSpec, make_stripe_inputs, round_to_bf16_bits
+
+
+def bits(x):
+    return round_to_bf16_bits(np.asarray(x, dtype=np.float32))
+
+
+def _rng(seed=7):
+    return np.random.Generator(np.random.PCG64(seed))
+
+
+def _stripe(B=1, Hq=2, Hkv=1, N=512, d=64, seed=11, **kw):
+    spec = StripeSpec(B, Hq, Hkv, N, d, n_vert=kw.get("n_vert", 8),
+                      n_horiz=kw.get("n_horiz", 4),
+                      window=kw.get("window", 32), seed=seed)
+    return make_stripe_inputs(spec)
+
+
+# ---------------------------------------------------------------- inputs
+
+def check_fixed_point(O):
+    # 256 x rounded half to even, saturated to int16
+    vals = [1.0, -1.0, 0.5, 2.0 ** -9, 3 * 2.0 ** -9, 5 * 2.0 ** -9,
+            -3 * 2.0 ** -9, 200.0, -200.0, 127.5, 0.333984375, 0.0]
+    want = [256, -256, 128, 0, 2, 2, -2, 32767, -32768, 32640, 86, 0]
+    got = O.fixed_point(bits(vals))
+    assert got.dtype == np.int64
+    assert list(got) == want, (list(got), want)
+
+
+# ---------------------------------------------------------------- dense
+
+def check_dense_vs_sdpa(O):
+    rng = _rng(1)
+    for Hq, Hkv, N, d in [(2, 1, 70, 16), (4, 2, 33, 64)]:
+        q = bits(2 * rng.standard_normal((1, Hq, N, d)))
+        k = bits(2 * rng.standard_normal((1, Hkv, N, d)))
+        v = bits(rng.standard_normal((1, Hkv, N, d)))
+        o, lse = O.dense_causal(q, k, v)
+        G = Hq // Hkv
+        tq = torch.from_numpy(O.decode_bf16(q))
+        tk = torch.from_numpy(O.decode_bf16(k)).repeat_interleave(G, 1)
+        tv = torch.from_numpy(O.decode_bf16(v)).repeat_interleave(G, 1)
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            tq, tk, tv, is_causal=True).numpy()
+        assert np.abs(o - ref).max() < 1e-12
+        # lse against torch.logsumexp over the causal logits
+        z = torch.einsum("bhid,bhjd->bhij", tq, tk) / math.sqrt(d)
+        z = z.masked_fill(torch.ones(N, N, dtype=torch.bool).triu(1),
+                          float("-inf"))
+        assert np.abs(lse - torch.logsumexp(z, -1).numpy()).max() < 1e-12
+
+
+def check_dense_closed_forms(O):
+    rng = _rng(2)
+    N, d = 48, 16
+    q = bits(rng.standard_normal((1, 1, N, d)))
+    k = np.broadcast_to(bits(rng.standard_normal((1, 1, 1, d))),
+                        (1, 1, N, d)).copy()
+    v = bits(rng.standard_normal((1, 1, N, d)))
+    o, lse = O.dense_causal(q, k, v)
+    v64 = O.decode_bf16(v)[0, 0]
+    ref = np.cumsum(v64, 0) / np.arange(1, N + 1)[:, None]
+    assert np.abs(o[0, 0] - ref).max() < 1e-13
+    z = O.decode_bf16(q)[0, 0] @ O.decode_bf16(k)[0, 0, 0] / math.sqrt(d)
+    assert np.abs(lse[0, 0] - z - np.log(np.arange(1, N + 1))).max() < 1e-12
+
+
+# ---------------------------------------------------------------- orders
+
+def _worked_inputs(extra_prefix_keys: bool):
+    """N = 256, S = 64, d = 8, one head; answers derived by hand below."""
+    N, d = 256, 8
+    qf = np.zeros((1, 1, N, d))
+    qf[0, 0, :, 0] = 1.0
+    m = (np.arange(64) * 37) % 64                 # a permutation of 0..63
+    qf[0, 0, 128:192, 1] = (2 * m - 63) / 128.0   # zero-sum, exact in bf16
+    kf = np.zeros((1, 1, N, d))
+    for j, a in [(5, 2.0), (70, 1.5), (130, 1.0), (200, 0.5)]:
+        kf[0, 0, j, 0] = a
+    kf[0, 0, 70, 1] = 1.0
+    if extra_prefix_keys:
+        kf[0, 0, [100, 101, 102], 1] = 1.0
+    return bits(qf), bits(kf), m
+
+
+def check_worked_orders(O):
+    """Hand-derived orders.
+
+    fx(q_i) = (256, 4 m_i - 126 in segment 2 else 0, 0...), so the pooled
+    query is P = (65536, 0, ...) and v_j = 65536 * 256 * a_j: keys 5, 70,
+    130, 200 rank first in that order, all other keys tie at 0 and follow in
+    index order. Segment 1: its top tile is all of segment 0, which is also
+    its whole prefix, so C_1 = 0 and the order is the identity. Segment 2:
+    the top tile of L_2 holds keys 5 and 70, the prefix keys 0..127; the
+    second coordinate of C_2 = 128 * top - 64 * prefix is 128 * 256 -
+    64 * 256 > 0 with only key 70 carrying it, so queries rank by m
+    descending; with keys 100..102 also carrying it (prefix only) it is
+    128 * 256 - 64 * 1024 < 0 and queries rank by m ascending. Segment 3's
+    queries are identical in the first coordinate and zero elsewhere:
+    identity.
+    """
+    for extra in (False, True):
+        q, k, m = _worked_inputs(extra)
+        pl = O.plan(q, k, 64)
+        hot = [5, 70, 130, 200]
+        rest = [j for j in range(256) if j not in hot]
+        assert list(pl.pi_k[0, 0]) == hot + rest
+        assert list(O.restricted_list(pl, 0, 0, 1)) == [5] + [
+            j for j in range(64) if j != 5]
+        assert list(O.restricted_list(pl, 0, 0, 2)) == [5, 70] + [
+            j for j in range(128) if j not in (5, 70)]
+        assert list(O.restricted_list(pl, 0, 0, 3)) == [5, 70, 130] + [
+            j for j in range(192) if j not in (5, 70, 130)]
+        pq = pl.pi_q[0, 0]
+        assert list(pq[:128]) == list(range(128))
+        assert list(pq[192:]) == list(range(192, 256))
+        local = sorted(range(64), key=(lambda i: m[i]) if extra
+                       else (lambda i: -m[i]))
+        assert list(pq[128:192]) == [128 + i for i in local]
+
+
+def check_stripe_score_bruteforce(O):
+    """v_j = column sum of the integer logit matrix over all group queries
+    (the mean-pooled vertical stripe, up to the factor G N); the orders equal
+    ranks obtained by pairwise counting."""
+    q, k, _ = _stripe(Hq=2, Hkv=1, N=256, d=16, seed=3)
+    pl = O.plan(q, k, 64)
+    qx = [O.fixed_point(q[0, h]) for h in range(2)]
+    kx = O.fixed_point(k[0, 0])
+    col = sum((x @ kx.T).sum(axis=0) for x in qx)
+    assert np.array_equal(pl.key_score[0, 0], col)
+    v = [int(x) for x in col]
+    rank = [sum(1 for j2 in range(256) if (v[j2], -j2) > (v[j], -j))
+            for j in range(256)]
+    inv = np.empty(256, dtype=np.int64)
+    inv[rank] = np.arange(256)
+    assert np.array_equal(pl.pi_k[0, 0], inv)
+    # query scores: u_i = 64 t S (q_i . mean(top tile) - q_i . mean(prefix))
+    S = 64
+    for h in range(2):
+        for t in (1, 3):
+            Lt = O.restricted_list(pl, 0, 0, t)
+            top = [Fraction(int(x), 64) for x in kx[Lt[:64]].sum(axis=0)]
+            pre = [Fraction(int(x), t * S) for x in kx[:t * S].sum(axis=0)]
+            for i in range(t * S, t * S + S, 7):
+                qi = [int(x) for x in qx[h][i]]
+                u = 64 * t * S * (sum(a * b for a, b in zip(qi, top))
+                                  - sum(a * b for a, b in zip(qi, pre)))
+                assert u.denominator == 1
+                assert int(u) == pl.query_score[0, h, i]
+
+
+def check_plan_invariants(O):
+    q, k, _ = _stripe(Hq=4, Hkv=2, N=1024, d=32, seed=4)
+    S = 256
+    for flags in (0, O.SA_NO_QPERM, O.SA_NO_KVPERM):
+        pl = O.plan(q, k, S, flags=flags)
+        for g in range(2):
+            pk = pl.pi_k[0, g]
+            assert np.array_equal(np.sort(pk), np.arange(1024))
+            pos = np.empty(1024, dtype=np.int64)
+            pos[pk] = np.arange(1024)
+            for t in range(1, 4):
+                Lt = O.restricted_list(pl, 0, g, t)
+                assert len(Lt) == t * S
+                assert np.array_equal(np.sort(Lt), np.arange(t * S))
+                assert np.all(np.diff(pos[Lt]) > 0)    # subsequence of pi_K
+        for h in range(4):
+            pq = pl.pi_q[0, h]
+            for t in range(4):
+                seg = pq[t * S:(t + 1) * S]
+                assert np.array_equal(np.sort(seg), np.arange(t * S,
+                                                              (t + 1) * S))
+            assert np.array_equal(pq[:S], np.arange(S))   # u = 0 there
+        if flags & O.SA_NO_QPERM:
+            assert np.array_equal(pl.pi_q[0, 0], np.arange(1024))
+        if flags & O.SA_NO_KVPERM:
+            assert np.array_equal(pl.pi_k[0, 0], np.arange(1024))
+
+
+# ---------------------------------------------------------------- S2O
+
+def check_tau0_is_dense(O):
+    q, k, v = _stripe(Hq=2, Hkv=1, N=512, d=64, seed=5)
+    od, ld = O.dense_causal(q, k, v)
+    for flags in (0, O.SA_NO_QPERM, O.SA_NO_KVPERM,
+                  O.SA_NO_QPERM | O.SA_NO_KVPERM):
+        o, lse, *_ = O.s2o_attention(q, k, v, 128, 0.0, flags)
+        assert np.abs(o - od).max() < 1e-12
+        assert np.abs(lse - ld).max() < 1e-12
+    o, *_ = O.s2o_attention(q, k, v, 128, 0.3, O.SA_NO_EARLYSTOP)
+    assert np.abs(o - od).max() < 1e-12
+
+
+def check_kv_order_invariance(O):
+    q, k, v = _stripe(Hq=2, Hkv=1, N=512, d=32, seed=6)
+    od, _ = O.dense_causal(q, k, v)
+    perm = _rng(9).permutation(512)[None, None]
+    pl = O.plan(q, k, 128, kv_order=perm)
+    n_I, _ = O.stop_points(q, k, pl, 0.0)
+    o, _ = O.attend(q, k, v, pl, n_I)
+    assert np.abs(o - od).max() < 1e-12
+
+
+def check_single_segment_is_dense(O):
+    q, k, v = _stripe(Hq=2, Hkv=1, N=256, d=32, seed=8)
+    od, _ = O.dense_causal(q, k, v)
+    o, _, _, n_I, _ = O.s2o_attention(q, k, v, 256, 0.5)
+    assert np.all(n_I == 0)
+    assert np.abs(o - od).max() < 1e-12
+
+
+def check_bruteforce_restricted(O):
+    """Row-by-row attention over an explicitly built key set equals the
+    block computation: Sel(i) = own-segment keys j <= i plus the first n_I
+    tiles of L_t (brute force, per row, no blocks)."""
+    q, k, v = _stripe(Hq=2, Hkv=1, N=384, d=16, seed=10)
+    S = 128
+    pl = O.plan(q, k, S)
+    n_I, _ = O.stop_points(q, k, pl, 0.3)
+    full = (np.arange(6) // 2) * 2            # t S / 64 tiles per block
+    assert np.any((n_I[0] > 0) & (n_I[0] < full))   # some blocks stop early
+    o, lse = O.attend(q, k, v, pl, n_I)
+    q64, k64, v64 = (O.decode_bf16(x) for x in (q, k, v))
+    for h in range(2):
+        block_of_row = np.empty(384, dtype=np.int64)
+        block_of_row[pl.pi_q[0, h]] = np.arange(384) // 64
+        for i in range(0, 384, 5):
+            t = i // S
+            sel = [j for j in range(t * S, i + 1)]
+            n = int(n_I[0, h, block_of_row[i]])
+            if t > 0:
+                order = [int(j) for j in pl.pi_k[0, 0] if j < t * S]
+                sel += order[:64 * n]
+            z = np.array([q64[0, h, i] @ k64[0, 0, j] for j in sel]) / 4.0
+            w = np.exp(z - z.max())
+            ref = (w[:, None] * v64[0, 0, sel]).sum(0) / w.sum()
+            assert np.abs(o[0, h, i] - ref).max() < 1e-12
+            assert abs(lse[0, h, i] - (z.max() + np.log(w.sum()))) < 1e-12
+
+
+def _closed_form_n(tau, D, t, S, r=1.0):
+    """First k with r/(D/4096 + r (k + 1)) < tau, for E_diag = (D/64) e^s0
+    and E_k = 64 e^s1, r = e^(s1 - s0): k > 1/tau - D/(4096 r) - 1."""
+    x = 1.0 / tau - D / (4096.0 * r)
+    frac = x - math.floor(x)
+    assert 1e-9 < frac < 1 - 1e-9, "case too close to a tie for a pin"
+    return min(t * S // 64, max(0, math.floor(x)))
+
+
+def check_constant_keys_closed_form(O):
+    """All keys equal: both orders are the identity (every v_j ties, C_t = 0)
+    and every estimate is the same s, so p_k = 64 / (D_I / 64 + 64 (k + 1))
+    with D_I = sum_{i in I} (i - t S + 1): n_I = min(t S / 64,
+    max(0, floor(1/tau - D_I / 4096))). At exact equality p_k = tau the
+    block is still visited (the comparison is strict)."""
+    N, d, S = 512, 32, 128
+    rng = _rng(12)
+    q = bits(rng.standard_normal((1, 1, N, d)))
+    v = bits(rng.standard_normal((1, 1, N, d)))
+    for kvec in (np.zeros(d), rng.standard_normal(d)):
+        k = np.broadcast_to(bits(kvec), (1, 1, N, d)).copy()
+        for tau in (0.05, 0.013, 0.125, 0.0625, 1.0, 0.0):
+            if tau == 1.0 and kvec.any():
+                continue
+            pl = O.plan(q, k, S)
+            assert np.array_equal(pl.pi_k[0, 0], np.arange(N))
+            assert np.array_equal(pl.pi_q[0, 0], np.arange(N))
+            n_I, _ = O.stop_points(q, k, pl, tau)
+            for I in range(N // 64):
+                t = I * 64 // S
+                D = sum(i - t * S + 1 for i in range(64 * I, 64 * I + 64))
+                want = 0 if t == 0 else (
+                    t * S // 64 if tau == 0 else _closed_form_n(tau, D, t, S))
+                assert n_I[0, 0, I] == want, (tau, I, n_I[0, 0, I], want)
+            # with identical keys the output is the uniform mean over Sel(i)
+            if tau == 0.05:
+                o, _ = O.attend(q, k, v, pl, n_I)
+                v64 = O.decode_bf16(v)[0, 0]
+                for i in (130, 300, 511):
+                    t = i // S
+                    n = int(n_I[0, 0, i // 64])
+                    sel = list(range(t * S, i + 1)) + list(range(64 * n))
+                    ref = v64[sel].mean(axis=0)
+                    assert np.abs(o[0, 0, i] - ref).max() < 1e-12
+
+
+def check_strict_stop(O):
+    """At exact equality p_k = tau the tile is still visited. With zero keys
+    every estimate is exp(0) = 1; 64 rows at t S + 63 see all 64 keys of the
+    first local block, so E_diag = 64 and p_k = 64 / (64 + 64 (k + 1)) =
+    1 / (k + 2): with tau = 1/4, p_2 = tau is visited and k = 3 stops."""
+    S, d = 128, 16
+    k64 = np.zeros((2 * S, d))
+    rows = np.full(64, S + 63)
+    Lt = np.arange(S)
+    n, ps = O.block_stop(np.ones(d), rows, 1, k64, Lt, S, 0.25,
+                         1.0 / math.sqrt(d))
+    assert n == 2 and list(ps) == [0.5, 1 / 3]   # only 2 tiles exist
+    Lt = np.arange(2 * S)
+    k64 = np.zeros((3 * S, d))
+    n, ps = O.block_stop(np.ones(d), np.full(64, 2 * S + 63), 2, k64, Lt,
+                         S, 0.25, 1.0 / math.sqrt(d))
+    assert n == 3 and list(ps) == [0.5, 1 / 3, 0.25, 0.2]
+
+
+def check_two_level_closed_form(O):
+    """Segment 0 keys all equal a e_0, segment 1 keys zero (N = 2 S): for a
+    block of segment 1 the diagonal estimate is s0 = 0 and every tile's is
+    s1 = kappa * qbar_0 * a, so p_k = r / (D_I / 4096 + r (k + 1)) with
+    r = exp(s1): the closed form pins kappa, the mean pooling of the query
+    block and the 64 keys per row of a sparse tile."""
+    N, d, S = 256, 16, 128
+    rng = _rng(13)
+    qf = rng.standard_normal((1, 1, N, d))
+    qf[0, 0, :, 0] += 1.5
+    kf = np.zeros((1, 1, N, d))
+    kf[0, 0, :S, 0] = 2.0
+    q, k = bits(qf), bits(kf)
+    pl = O.plan(q, k, S)
+    q64 = O.decode_bf16(q)[0, 0]
+    assert np.array_equal(pl.pi_q[0, 0, S:], np.arange(S, N))
+    for tau in (0.02, 0.04, 0.09):
+        n_I, _ = O.stop_points(q, k, pl, tau)
+        for I in range(S // 64, N // 64):
+            rows = pl.pi_q[0, 0, 64 * I:64 * I + 64]
+            D = int((rows - S + 1).sum())
+            r = math.exp(q64[rows, 0].mean() * 2.0 / math.sqrt(d))
+            assert n_I[0, 0, I] == _closed_form_n(tau, D, 1, S, r), tau
+
+
+def check_permuted_block_closed_form(O):
+    """Two-tile closed form on a permuted query block (N = 2 S, S = 128).
+
+    Segment 0 keys are (1, +1/2, 0...) for the 64 keys of H (odd j) and
+    (1, -1/2, 0...) for the others; segment 1 keys are zero. Queries are
+    (1, c_i, 0...) with c_i > 0, so P_1 > 0 and the H keys rank first: tile 0
+    of L_1 is H (mean (1, 1/2)), tile 1 the rest (mean (1, -1/2)). Then
+    C_1 = 128 * top - 64 * prefix = (0, 2^20, 0...), so segment 1's queries
+    are ordered by c_i descending. For a block with rows R (that order),
+    qbar = (1, mean c over R); the local window has keys 0, so E_diag =
+    D / 64 with D = sum_{i in R} (i - S + 1); tile k has E_k = 64 r_k with
+    r_0 = exp(kappa (1 + qbar_1 / 2)), r_1 = exp(kappa (1 - qbar_1 / 2)).
+    n_I = 0 if r_0 / (D / 4096 + r_0) < tau, else 1 if
+    r_1 / (D / 4096 + r_0 + r_1) < tau, else 2.
+    """
+    N, d, S = 256, 16, 128
+    m = (np.arange(128) * 45) % 128               # a permutation of 0..127
+    c = np.full(N, 0.5)
+    c[S:] = (m + 1) / 64.0                        # exact in bf16
+    qf = np.zeros((1, 1, N, d))
+    qf[0, 0, :, 0] = 1.0
+    qf[0, 0, :, 1] = c
+    kf = np.zeros((1, 1, N, d))
+    kf[0, 0, :S, 0] = 1.0
+    kf[0, 0, :S, 1] = np.where(np.arange(S) % 2 == 1, 0.5, -0.5)
+    q, k = bits(qf), bits(kf)
+    pl = O.plan(q, k, S)
+    order = sorted(range(S, N), key=lambda i: (-c[i], i))
+    assert list(pl.pi_q[0, 0, S:]) == order
+    kap = 1.0 / math.sqrt(d)
+    seen = set()
+    for tau in np.linspace(0.05, 0.6, 23):
+        n_I, _ = O.stop_points(q, k, pl, float(tau))
+        for blk in (0, 1):
+            R = np.array(order[64 * blk:64 * blk + 64])
+            D = float((R - S + 1).sum())
+            qb1 = c[R].mean()
+            r0 = math.exp(kap * (1 + qb1 / 2))
+            r1 = math.exp(kap * (1 - qb1 / 2))
+            if r0 / (D / 4096 + r0) < tau:
+                want = 0
+            elif r1 / (D / 4096 + r0 + r1) < tau:
+                want = 1
+            else:
+                want = 2
+            assert n_I[0, 0, 2 + blk] == want, (tau, blk)
+            seen.add((blk, want))
+    assert len(seen) >= 5          # the grid exercises every outcome
+
+
+def check_monotone_tau(O):
+    q, k, _ = _stripe(Hq=2, Hkv=1, N=1024, d=32, seed=14)
+    pl = O.plan(q, k, 256)
+    prev = None
+    for tau in (0.0, 0.002, 0.01, 0.03, 0.1, 1.0):
+        n_I, _ = O.stop_points(q, k, pl, tau)
+        if prev is not None:
+            assert np.all(n_I <= prev)
+        prev = n_I
+    assert np.all(prev == 0)
+
+
+ALL_CHECKS = [
+    check_fixed_point, check_dense_vs_sdpa, check_dense_closed_forms,
+    check_worked_orders, check_stripe_score_bruteforce, check_plan_invariants,
+    check_tau0_is_dense, check_kv_order_invariance,
+    check_single_segment_is_dense, check_bruteforce_restricted,
+    check_constant_keys_closed_form, check_strict_stop,
+    check_two_level_closed_form, check_permuted_block_closed_form,
+    check_monotone_tau,
+]

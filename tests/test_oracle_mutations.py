@@ -1,0 +1,79 @@
+"""The pins are strong enough: each planted mistake in a copy of the oracle
+makes at least one pin fail (mistakes are planted on the CPU, in the copy
+only; the real oracle is untouched)."""
+import pathlib
+import sys
+import types
+
+import pytest
+
+import oracle.s2o as S2O
+from tests import oracle_pins as P
+
+SRC = pathlib.Path(S2O.__file__).read_text()
+
+# (name, exact text in oracle/s2o.py, replacement)
+MUTANTS = [
+    ("floor_not_rint", "y = np.rint(x * 256.0)", "y = np.floor(x * 256.0)"),
+    ("scale_128", "y = np.rint(x * 256.0)", "y = np.rint(x * 128.0)"),
+    ("clip_bounds", "np.clip(y, -32768.0, 32767.0)",
+     "np.clip(y, -32767.0, 32767.0)"),
+    ("kv_ascending", "order = np.lexsort((idx, -v))",
+     "order = np.lexsort((idx, v))"),
+    ("kv_tie_desc", "order = np.lexsort((idx, -v))",
+     "order = np.lexsort((-idx, -v))"),
+    ("q_ascending", "np.lexsort((seg, -u[seg]))]", "np.lexsort((seg, u[seg]))]"),
+    ("drop_prefix", "(t * S) * top - BLOCK * prefix", "(t * S) * top"),
+    ("swap_factors", "(t * S) * top - BLOCK * prefix",
+     "BLOCK * top - (t * S) * prefix"),
+    ("top_from_prefix", "top = kx[Lt[:BLOCK]].sum(axis=0)",
+     "top = kx[:BLOCK].sum(axis=0)"),
+    ("restrict_le", "Lt = order[order < t * S]",
+     "Lt = order[order <= t * S][:t * S]"),
+    ("stop_le", "if p < tau:", "if p <= tau:"),
+    ("diag_weight", "acc += (nv / BLOCK) * math.exp", "acc += nv * math.exp"),
+    ("tile_mass_1", "E = BLOCK * np.exp(kap * (kbar @ qbar))",
+     "E = np.exp(kap * (kbar @ qbar))"),
+    ("no_running_sum", "        acc += E[kk]\n", "\n"),
+    ("estimate_no_kappa", "E = BLOCK * np.exp(kap * (kbar @ qbar))",
+     "E = BLOCK * np.exp(kbar @ qbar)"),
+    ("ratio_without_self", "p = E[kk] / (acc + E[kk])", "p = E[kk] / acc"),
+    ("qbar_natural_rows", "qbar = q64[rows].mean(axis=0)",
+     "qbar = q64[I * BLOCK:(I + 1) * BLOCK].mean(axis=0)"),
+    ("nvis_clip63", "np.clip(rows - j0 + 1, 0, BLOCK)",
+     "np.clip(rows - j0, 0, BLOCK)"),
+    ("dense_kappa_1_over_d", "return 1.0 / math.sqrt(d)", "return 1.0 / d"),
+    ("dense_mask_ge", "z[np.arange(N)[None, :] > r[:, None]] = -np.inf",
+     "z[np.arange(N)[None, :] >= r[:, None]] = -np.inf"),
+    ("attend_mask_ge", "z[:, :S][local[None, :] > rows[:, None]] = -np.inf",
+     "z[:, :S][local[None, :] >= rows[:, None]] = -np.inf"),
+    ("attend_one_more_tile", "[:n * BLOCK] if t > 0", "[:(n + 1) * BLOCK] if t > 0"),
+    ("attend_lse_no_max", "lse[b, h, rows] = (m + np.log(s))[:, 0]",
+     "lse[b, h, rows] = np.log(s)[:, 0]"),
+]
+
+
+def load_mutant(name, old, new):
+    assert SRC.count(old) == 1, f"{name}: anchor text not unique/present"
+    mod = types.ModuleType(f"oracle_mutant_{name}")
+    mod.__file__ = f"<mutant {name}>"
+    sys.modules[mod.__name__] = mod
+    try:
+        exec(compile(SRC.replace(old, new), mod.__file__, "exec"),
+             mod.__dict__)
+    finally:
+        del sys.modules[mod.__name__]
+    return mod
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_is_caught(name, old, new):
+    mod = load_mutant(name, old, new)
+    caught = []
+    for check in P.ALL_CHECKS:
+        try:
+            check(mod)
+        except (AssertionError, ValueError, IndexError):
+            caught.append(check.__name__)
+            break
+    assert caught, f"planted mistake '{name}' passed every pin"

@@ -21,7 +21,7 @@ the same readings are used by the GPU path.
 from __future__ import annotations
 
 import math
-from dataclasses import dataclass, field
+from dataclasses import dataclass
 from typing import Dict, Optional, Sequence, Tuple
 
 import numpy as np
@@ -121,7 +121,6 @@ class Plan:
     query_score: np.ndarray   # u [B, Hq, N] int64
     pi_q: np.ndarray          # [B, Hq, N] segment-local query order
     L: np.ndarray             # [B, Hkv, S*T*(T-1)/2] restricted lists, t = 1..T-1
-    _cache: Dict = field(default_factory=dict, repr=False)
 
     @property
     def n_segments(self) -> int:
@@ -258,12 +257,9 @@ def plan(q_bits, k_bits, segment: int, block: int = BLOCK,
 # Stop points (mean-pooled block estimates and the tau test)
 # --------------------------------------------------------------------------
 
-def _keys64(k_bits, pl: Plan, b: int, g: int) -> np.ndarray:
-    key = ("k", b, g)
-    if key not in pl._cache:
-        pl._cache.clear()
-        pl._cache[key] = decode_bf16(k_bits[b, g])
-    return pl._cache[key]
+def block_means(k64: np.ndarray, keys: np.ndarray) -> np.ndarray:
+    """Mean key of every consecutive 64-key tile of ``keys`` (float64)."""
+    return k64[keys].reshape(len(keys) // BLOCK, BLOCK, -1).mean(axis=1)
 
 
 def n_visible(rows: np.ndarray, j0: int) -> int:
@@ -271,8 +267,9 @@ def n_visible(rows: np.ndarray, j0: int) -> int:
     return int(np.clip(rows - j0 + 1, 0, BLOCK).sum())
 
 
-def block_stop(qbar: np.ndarray, rows: np.ndarray, t: int, k64: np.ndarray,
-               Lt: Optional[np.ndarray], S: int, tau: float, kap: float):
+def block_stop(qbar: np.ndarray, rows: np.ndarray, t: int,
+               local_means: np.ndarray, tile_means: Optional[np.ndarray],
+               S: int, tau: float, kap: float):
     """Stop point n_I of one query block and the ratios it was decided on.
 
     S2O summary, Summary: blocks are processed from most to least important
@@ -293,6 +290,8 @@ def block_stop(qbar: np.ndarray, rows: np.ndarray, t: int, k64: np.ndarray,
         Acc_0 = E_diag and Acc_{k+1} = Acc_k + E_k;
       * stop at the first k with p_k < tau (strict); n_I = that k, or all
         t S / 64 tiles when none fails. tau = 0 never stops.
+    ``local_means`` holds the mean key of the segment's 64-key blocks,
+    ``tile_means`` the mean key of the tiles of L_t in visiting order.
     Returns (n_I, p) where p holds p_0 .. p_{min(n_I, n_tiles - 1)}.
     """
     if t == 0:
@@ -300,24 +299,19 @@ def block_stop(qbar: np.ndarray, rows: np.ndarray, t: int, k64: np.ndarray,
     # dense local window estimate, blocks in ascending order
     acc = 0.0
     for c in range(S // BLOCK):
-        j0 = t * S + c * BLOCK
-        nv = n_visible(rows, j0)
+        nv = n_visible(rows, t * S + c * BLOCK)
         if nv > 0:
-            kbar = k64[j0:j0 + BLOCK].mean(axis=0)
-            acc += (nv / BLOCK) * math.exp(kap * float(qbar @ kbar))
-    n_tiles = len(Lt) // BLOCK
-    # tile means in visiting order; estimates past the stop point are
-    # computed but never used
-    kbar = k64[Lt].reshape(n_tiles, BLOCK, -1).mean(axis=1)
-    E = BLOCK * np.exp(kap * (kbar @ qbar))
+            acc += (nv / BLOCK) * math.exp(kap * float(qbar @ local_means[c]))
+    # estimates past the stop point are computed but never used
+    E = BLOCK * np.exp(kap * (tile_means @ qbar))
     ps = []
-    for kk in range(n_tiles):
+    for kk in range(len(tile_means)):
         p = E[kk] / (acc + E[kk])
         ps.append(p)
         if p < tau:
             return kk, np.asarray(ps)
         acc += E[kk]
-    return n_tiles, np.asarray(ps)
+    return len(tile_means), np.asarray(ps)
 
 
 def stop_points(q_bits, k_bits, pl: Plan, tau: float,
@@ -339,19 +333,24 @@ def stop_points(q_bits, k_bits, pl: Plan, tau: float,
     if blocks is None:
         blocks = [(b, h, I) for b in range(B) for h in range(Hq)
                   for I in range(nb)]
-    by_head: Dict[Tuple[int, int], list] = {}
+    by_group: Dict[Tuple[int, int, int], list] = {}
     for b, h, I in blocks:
-        by_head.setdefault((b, h), []).append(I)
-    for (b, h), Is in sorted(by_head.items()):
-        g = h // G
-        k64 = _keys64(k_bits, pl, b, g)
-        q64 = decode_bf16(q_bits[b, h])
-        for I in Is:
+        by_group.setdefault((b, h // G, (I * BLOCK) // S), []).append((h, I))
+    q_cache: Dict[Tuple[int, int], np.ndarray] = {}
+    for (b, g, t), items in sorted(by_group.items()):
+        k64 = decode_bf16(k_bits[b, g])
+        local_means = block_means(k64, np.arange(t * S, (t + 1) * S))
+        tile_means = (block_means(k64, restricted_list(pl, b, g, t))
+                      if t > 0 else None)
+        for h, I in items:
+            if (b, h) not in q_cache:
+                q_cache.clear()
+                q_cache[(b, h)] = decode_bf16(q_bits[b, h])
+            q64 = q_cache[(b, h)]
             rows = pl.pi_q[b, h, I * BLOCK:(I + 1) * BLOCK]
-            t = (I * BLOCK) // S
             qbar = q64[rows].mean(axis=0)
-            Lt = restricted_list(pl, b, g, t) if t > 0 else None
-            n, ps = block_stop(qbar, rows, t, k64, Lt, S, tau, kap)
+            n, ps = block_stop(qbar, rows, t, local_means, tile_means, S,
+                               tau, kap)
             n_I[b, h, I] = n
             traces[(b, h, I)] = ps
     return n_I, traces

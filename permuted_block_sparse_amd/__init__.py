@@ -1,0 +1,203 @@
+"""Permuted, early-stopping block-sparse causal prefill attention on MI355X.
+
+Thin Python binding over libsparse_attn.so (include/sparse_attn.h). torch is
+used only to own device memory and to supply the current HIP stream; every
+step of the computation runs in the library's gfx950 kernels. There is no
+CPU fallback: without the built library every call raises.
+
+    pl = plan(q, k, segment=2048, tau=0.005)    # estimator + index builder
+    o = prefill(pl, q, k, v)                    # gather attention + stop
+    o, lse = prefill(pl, q, k, v, return_lse=True)
+
+q: [B, Hq, N, 128] bfloat16 CUDA tensor; k, v: [B, Hkv, N, 128].
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional
+
+import numpy as np
+import torch
+
+from . import _lib
+from ._lib import (SA_NO_QPERM, SA_NO_KVPERM, SA_NO_EARLYSTOP,
+                   SparseAttnError)
+
+__all__ = ["plan", "prefill", "SparsePlan", "SA_NO_QPERM", "SA_NO_KVPERM",
+           "SA_NO_EARLYSTOP", "SparseAttnError", "workspace_bytes"]
+
+_EXPORT_DTYPES = {
+    _lib.SA_EXPORT_PI_K: np.int32, _lib.SA_EXPORT_PI_Q: np.int32,
+    _lib.SA_EXPORT_L: np.int32, _lib.SA_EXPORT_N_I: np.int32,
+    _lib.SA_EXPORT_KEY_SCORE: np.int64, _lib.SA_EXPORT_QUERY_SCORE: np.int64,
+    _lib.SA_EXPORT_CONTRAST: np.int64, _lib.SA_EXPORT_POOLED: np.int64,
+}
+
+
+def _stream_ptr(stream: Optional[torch.cuda.Stream]) -> int:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def _check_tensor(x: torch.Tensor, name: str, heads_dim_ok=True):
+    if not isinstance(x, torch.Tensor) or not x.is_cuda:
+        raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+    if x.dtype != torch.bfloat16:
+        raise TypeError(f"{name} must be bfloat16")
+    if x.dim() != 4 or not x.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous 4-D tensor")
+
+
+def _params(q, k, segment, tau, block, flags) -> _lib.SaParams:
+    B, Hq, N, d = q.shape
+    return _lib.SaParams(B, Hq, k.shape[1], N, d, segment, block, float(tau),
+                         int(flags))
+
+
+def workspace_bytes(batch, heads_q, heads_kv, seq_len, segment, head_dim=128,
+                    block=64, tau=0.0, flags=0) -> int:
+    lib = _lib.load()
+    p = _lib.SaParams(batch, heads_q, heads_kv, seq_len, head_dim, segment,
+                      block, float(tau), int(flags))
+    return int(lib.sparse_attn_workspace_bytes(ctypes.byref(p)))
+
+
+class SparsePlan:
+    """A plan (index arrays in a device workspace owned by this object)."""
+
+    def __init__(self, q, k, segment, tau, block=64, flags=0, stream=None):
+        lib = _lib.load()
+        _check_tensor(q, "q")
+        _check_tensor(k, "k")
+        if q.shape[0] != k.shape[0] or q.shape[2:] != k.shape[2:]:
+            raise ValueError("q and k shapes do not agree")
+        self.params = _params(q, k, segment, tau, block, flags)
+        nbytes = lib.sparse_attn_workspace_bytes(ctypes.byref(self.params))
+        if nbytes == 0:
+            raise SparseAttnError(_lib.SA_ERR_UNSUPPORTED_SHAPE,
+                                  "sparse_attn_workspace_bytes")
+        self.workspace = torch.empty(nbytes + 256, dtype=torch.uint8,
+                                     device=q.device)
+        base = self.workspace.data_ptr()
+        self._ws_ptr = (base + 255) // 256 * 256
+        self._handle = ctypes.c_void_p()
+        self.shape = tuple(q.shape)
+        self.heads_kv = k.shape[1]
+        self._inputs = (q, k)   # the plan keeps device pointers to both
+        st = lib.sparse_attn_plan(
+            ctypes.byref(self.params), ctypes.c_void_p(q.data_ptr()),
+            ctypes.c_void_p(k.data_ptr()), ctypes.c_void_p(self._ws_ptr),
+            ctypes.c_size_t(nbytes), ctypes.c_void_p(_stream_ptr(stream)),
+            ctypes.byref(self._handle))
+        _lib.check(st, "sparse_attn_plan")
+
+    @property
+    def tau(self) -> float:
+        return self.params.tau
+
+    def set_tau(self, tau: float) -> None:
+        _lib.check(_lib.load().sparse_attn_plan_set_tau(self._handle,
+                                                        float(tau)),
+                   "sparse_attn_plan_set_tau")
+        self.params.tau = float(tau)
+
+    def set_kv_order(self, pi_k: torch.Tensor, stream=None) -> None:
+        if pi_k.dtype != torch.int32 or not pi_k.is_cuda:
+            raise TypeError("pi_k must be an int32 CUDA tensor")
+        B, Hq, N, _ = self.shape
+        if tuple(pi_k.shape) != (B, self.heads_kv, N):
+            raise ValueError("pi_k must be [B, Hkv, N]")
+        pi_k = pi_k.contiguous()
+        _lib.check(_lib.load().sparse_attn_plan_set_kv_order(
+            self._handle, ctypes.c_void_p(pi_k.data_ptr()),
+            ctypes.c_void_p(_stream_ptr(stream))),
+            "sparse_attn_plan_set_kv_order")
+        self._keepalive = pi_k
+
+    def export(self, what: int, stream=None) -> np.ndarray:
+        lib = _lib.load()
+        n = lib.sparse_attn_plan_export_bytes(self._handle, what)
+        dt = _EXPORT_DTYPES[what]
+        out = np.empty(n // np.dtype(dt).itemsize, dtype=dt)
+        if n:
+            _lib.check(lib.sparse_attn_plan_export(
+                self._handle, what, out.ctypes.data_as(ctypes.c_void_p), n,
+                ctypes.c_void_p(_stream_ptr(stream))),
+                "sparse_attn_plan_export")
+        return out
+
+    def pi_k(self):
+        B, Hq, N, _ = self.shape
+        return self.export(_lib.SA_EXPORT_PI_K).reshape(B, self.heads_kv, N)
+
+    def pi_q(self):
+        B, Hq, N, _ = self.shape
+        return self.export(_lib.SA_EXPORT_PI_Q).reshape(B, Hq, N)
+
+    def n_I(self):
+        B, Hq, N, _ = self.shape
+        return self.export(_lib.SA_EXPORT_N_I).reshape(B, Hq, N // 64)
+
+    def restricted_lists(self):
+        B, Hq, N, _ = self.shape
+        return self.export(_lib.SA_EXPORT_L).reshape(B, self.heads_kv, -1)
+
+    def key_score(self):
+        B, Hq, N, _ = self.shape
+        return self.export(_lib.SA_EXPORT_KEY_SCORE).reshape(
+            B, self.heads_kv, N)
+
+    def query_score(self):
+        B, Hq, N, _ = self.shape
+        return self.export(_lib.SA_EXPORT_QUERY_SCORE).reshape(B, Hq, N)
+
+    def contrast(self):
+        B, Hq, N, _ = self.shape
+        T = N // self.params.segment
+        return self.export(_lib.SA_EXPORT_CONTRAST).reshape(
+            B, self.heads_kv, T, 128)
+
+    def pooled(self):
+        B = self.shape[0]
+        return self.export(_lib.SA_EXPORT_POOLED).reshape(B, self.heads_kv,
+                                                          128)
+
+    def close(self) -> None:
+        if getattr(self, "_handle", None) and self._handle.value:
+            _lib.load().sparse_attn_plan_destroy(self._handle)
+            self._handle = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def plan(q: torch.Tensor, k: torch.Tensor, segment: int, tau: float,
+         block: int = 64, flags: int = 0, stream=None) -> SparsePlan:
+    """Importance estimation and index building (sparse_attn_plan)."""
+    return SparsePlan(q, k, segment, tau, block, flags, stream)
+
+
+def prefill(pl: SparsePlan, q: torch.Tensor, k: torch.Tensor,
+            v: torch.Tensor, out: Optional[torch.Tensor] = None,
+            return_lse: bool = False, stream=None):
+    """Gather attention with the tau stop (sparse_attn_prefill)."""
+    lib = _lib.load()
+    for x, n in ((q, "q"), (k, "k"), (v, "v")):
+        _check_tensor(x, n)
+    if tuple(q.shape) != pl.shape or k.shape != v.shape:
+        raise ValueError("q/k/v shapes do not match the plan")
+    o = out if out is not None else torch.empty_like(q)
+    _check_tensor(o, "out")
+    lse = (torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+           if return_lse else None)
+    st = lib.sparse_attn_prefill(
+        pl._handle, ctypes.c_void_p(q.data_ptr()),
+        ctypes.c_void_p(k.data_ptr()), ctypes.c_void_p(v.data_ptr()),
+        ctypes.c_void_p(o.data_ptr()),
+        ctypes.c_void_p(lse.data_ptr() if lse is not None else 0),
+        ctypes.c_void_p(_stream_ptr(stream)))
+    _lib.check(st, "sparse_attn_prefill")
+    return (o, lse) if return_lse else o

@@ -1,0 +1,505 @@
+// Importance estimator and index builder of permuted block-sparse prefill
+// attention (S2O page, Summary: a segment-local query ordering and a global
+// key/value ordering ranked by stripe-level mean pooling, kept as index
+// arrays; no tensor is moved). Every score here is an exact integer built
+// from the fixed-point images fx(x) = clamp(rint(256 x), -32768, 32767), so
+// the orders do not depend on summation order and are bit-reproducible.
+//
+// All kernels are HBM-bound streaming passes (pooling, scoring), LDS sorts
+// or index compaction; none is a dense contraction, so none uses MFMA.
+
+#include "sa_device.h"
+#include "sa_launch.h"
+
+namespace sa {
+
+// --------------------------------------------------------------------------
+// Pooled group query: part[b, h, chunk, :] = sum of fx(q) over the chunk's
+// rows. 16 lanes cover one 256-byte row with 16-byte loads (coalesced), 16
+// rows per pass.
+// --------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_pool_q(const uint16_t* __restrict__ q,
+                                                int64_t* __restrict__ part,
+                                                int N, int nchunk) {
+  __shared__ int32_t red[16][kHeadDim];
+  const int blk = blockIdx.x;
+  const int bh = blk / nchunk, ch = blk % nchunk;
+  const int tid = threadIdx.x, c = tid & 15, r0 = tid >> 4;
+  const int row0 = ch * kPoolRows;
+  const int rows = min(kPoolRows, N - row0);
+  const uint16_t* base = q + ((size_t)bh * N + row0) * kHeadDim + c * 8;
+  int32_t acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  for (int r = r0; r < rows; r += 16) {
+    uint4 w = *reinterpret_cast<const uint4*>(base + (size_t)r * kHeadDim);
+    int32_t f[8];
+    fixed_point8(w, f);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] += f[e];
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) red[r0][c * 8 + e] = acc[e];
+  __syncthreads();
+  if (tid < kHeadDim) {
+    int64_t s = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s += red[i][tid];
+    part[(size_t)blk * kHeadDim + tid] = s;
+  }
+}
+
+// pooled[b, g, :] = sum over the G heads of group g and all chunks.
+__global__ __launch_bounds__(128) void k_pool_reduce(
+    const int64_t* __restrict__ part, int64_t* __restrict__ pooled, int Hq,
+    int Hkv, int nchunk) {
+  const int bg = blockIdx.x, b = bg / Hkv, g = bg % Hkv, G = Hq / Hkv;
+  const int d = threadIdx.x;
+  int64_t s = 0;
+  for (int h = g * G; h < (g + 1) * G; ++h) {
+    const int64_t* p = part + ((size_t)(b * Hq + h) * nchunk) * kHeadDim + d;
+    for (int ch = 0; ch < nchunk; ++ch) s += p[(size_t)ch * kHeadDim];
+  }
+  pooled[(size_t)bg * kHeadDim + d] = s;
+}
+
+// --------------------------------------------------------------------------
+// Key stripe score v_j = pooled . fx(k_j) (int64) and, on the same pass over
+// K, the per-64-row column sums of fx(k) (int32; |sum| <= 64 * 2^15).
+// --------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_key_score(
+    const uint16_t* __restrict__ k, const int64_t* __restrict__ pooled,
+    int64_t* __restrict__ vscore, int32_t* __restrict__ blocksum, int N,
+    int nwg) {
+  __shared__ int32_t red[4][16][kHeadDim];
+  const int bg = blockIdx.x / nwg, w = blockIdx.x % nwg;
+  const int tid = threadIdx.x, c = tid & 15, rr = tid >> 4;
+  const int row0 = w * kScoreRows;
+  const int rows = min(kScoreRows, N - row0);  // a multiple of 64
+  int64_t p8[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) p8[e] = pooled[(size_t)bg * kHeadDim + c * 8 + e];
+  const uint16_t* base = k + ((size_t)bg * N + row0) * kHeadDim + c * 8;
+  int32_t bs[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  for (int p = 0; p < 16; ++p) {
+    const int r = rr + 16 * p;
+    if (p * 16 < rows) {  // uniform over the workgroup
+      uint4 wv = *reinterpret_cast<const uint4*>(base + (size_t)r * kHeadDim);
+      int32_t f[8];
+      fixed_point8(wv, f);
+      int64_t dot = 0;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        dot += (int64_t)f[e] * p8[e];
+        bs[e] += f[e];
+      }
+      dot = sum16_i64(dot);
+      if (c == 0) vscore[(size_t)bg * N + row0 + r] = dot;
+    }
+    if ((p & 3) == 3) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        red[p >> 2][rr][c * 8 + e] = bs[e];
+        bs[e] = 0;
+      }
+    }
+  }
+  __syncthreads();
+  const int nblk = rows / kBlock;
+  for (int i = tid; i < 4 * kHeadDim; i += 256) {
+    const int bl = i / kHeadDim, d = i % kHeadDim;
+    if (bl < nblk) {
+      int32_t s = 0;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) s += red[bl][j][d];
+      blocksum[((size_t)bg * (N / kBlock) + row0 / kBlock + bl) * kHeadDim + d] =
+          s;
+    }
+  }
+}
+
+// segsum[b, g, t, :] = sum of fx(k) over segment t.
+__global__ __launch_bounds__(128) void k_segment_sum(
+    const int32_t* __restrict__ blocksum, int64_t* __restrict__ segsum, int N,
+    int S, int T) {
+  const int bgt = blockIdx.x, bg = bgt / T, t = bgt % T, d = threadIdx.x;
+  const int nb = S / kBlock;
+  const int32_t* p =
+      blocksum + ((size_t)bg * (N / kBlock) + (size_t)t * nb) * kHeadDim + d;
+  int64_t s = 0;
+  for (int i = 0; i < nb; ++i) s += p[(size_t)i * kHeadDim];
+  segsum[(size_t)bgt * kHeadDim + d] = s;
+}
+
+// --------------------------------------------------------------------------
+// Contrast vectors C_t = t S * sum_{j in L_t[0:64]} fx(k_j)
+//                       - 64 * sum_{j < t S} fx(k_j)     (t = 0: zero).
+// --------------------------------------------------------------------------
+__global__ __launch_bounds__(128) void k_contrast(
+    const uint16_t* __restrict__ k, const int32_t* __restrict__ L,
+    const int64_t* __restrict__ segsum, int64_t* __restrict__ contrast, int N,
+    int S, int T, long long list_len) {
+  const int bgt = blockIdx.x, bg = bgt / T, t = bgt % T, d = threadIdx.x;
+  int64_t c = 0;
+  if (t > 0) {
+    const int32_t* Lt = L + (size_t)bg * list_len + (size_t)S * t * (t - 1) / 2;
+    const uint16_t* kb = k + (size_t)bg * N * kHeadDim + d;
+    int64_t top = 0;
+    for (int r = 0; r < kBlock; ++r) {
+      const int key = min(max(Lt[r], 0), N - 1);  // memory-safe for any L
+      top += fixed_point(kb[(size_t)key * kHeadDim]);
+    }
+    int64_t pre = 0;
+    for (int s2 = 0; s2 < t; ++s2)
+      pre += segsum[((size_t)bg * T + s2) * kHeadDim + d];
+    c = (int64_t)t * S * top - (int64_t)kBlock * pre;
+  }
+  contrast[(size_t)bgt * kHeadDim + d] = c;
+}
+
+// Query stripe score u_i = fx(q_i) . C_seg(i) (C_0 = 0, so u = 0 there).
+__global__ __launch_bounds__(256) void k_query_score(
+    const uint16_t* __restrict__ q, const int64_t* __restrict__ contrast,
+    int64_t* __restrict__ u, int Hq, int Hkv, int N, int S, int T, int nwg) {
+  const int bh = blockIdx.x / nwg, w = blockIdx.x % nwg;
+  const int b = bh / Hq, h = bh % Hq, G = Hq / Hkv;
+  const int bg = b * Hkv + h / G;
+  const int tid = threadIdx.x, c = tid & 15, rr = tid >> 4;
+  const int row0 = w * kScoreRows;
+  const int rows = min(kScoreRows, N - row0);
+  const uint16_t* base = q + ((size_t)bh * N + row0) * kHeadDim + c * 8;
+  for (int p = 0; p * 16 < rows; ++p) {
+    const int r = rr + 16 * p;
+    const int t = (row0 + r) / S;
+    const int64_t* cv = contrast + ((size_t)bg * T + t) * kHeadDim + c * 8;
+    uint4 wv = *reinterpret_cast<const uint4*>(base + (size_t)r * kHeadDim);
+    int32_t f[8];
+    fixed_point8(wv, f);
+    int64_t dot = 0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) dot += (int64_t)f[e] * cv[e];
+    dot = sum16_i64(dot);
+    if (c == 0) u[(size_t)bh * N + row0 + r] = dot;
+  }
+}
+
+// --------------------------------------------------------------------------
+// Segmented argsort by (score descending, index ascending): bitonic sort of
+// chunks of up to 4096 elements in LDS, then merge-path merge passes. The
+// composite keys are unique, so the result does not depend on the algorithm.
+// --------------------------------------------------------------------------
+__device__ __forceinline__ void cmp_swap(uint64_t* key, int32_t* idx, int i,
+                                         int l, bool up) {
+  uint64_t ka = key[i], kb = key[l];
+  int32_t ia = idx[i], ib = idx[l];
+  const bool gt = pair_less(kb, ib, ka, ia);
+  if (gt == up) {
+    key[i] = kb; key[l] = ka;
+    idx[i] = ib; idx[l] = ia;
+  }
+}
+
+__global__ __launch_bounds__(256) void k_chunk_sort(
+    const int64_t* __restrict__ score, int seglen, int rowlen, int chunk,
+    int nch, int np2, uint64_t* __restrict__ okey, int32_t* __restrict__ oidx,
+    int32_t* __restrict__ out) {
+  __shared__ uint64_t key[kSortChunk];
+  __shared__ int32_t idx[kSortChunk];
+  const int seg = blockIdx.x / nch, ch = blockIdx.x % nch;
+  const int start = ch * chunk;
+  const int cnt = min(chunk, seglen - start);
+  const size_t gbase = (size_t)seg * seglen + start;
+  for (int i = threadIdx.x; i < np2; i += 256) {
+    if (i < cnt) {
+      key[i] = desc_key(score[gbase + i]);
+      idx[i] = (int32_t)((gbase + i) % (size_t)rowlen);
+    } else {
+      key[i] = ~0ull;
+      idx[i] = 0x7fffffff;
+    }
+  }
+  __syncthreads();
+  for (int kk = 2; kk <= np2; kk <<= 1) {
+    for (int j = kk >> 1; j > 0; j >>= 1) {
+      for (int p = threadIdx.x; p < (np2 >> 1); p += 256) {
+        const int i = (p / j) * 2 * j + (p % j);
+        cmp_swap(key, idx, i, i + j, (i & kk) == 0);
+      }
+      __syncthreads();
+    }
+  }
+  for (int i = threadIdx.x; i < cnt; i += 256) {
+    if (out != nullptr) {
+      out[gbase + i] = idx[i];
+    } else {
+      okey[gbase + i] = key[i];
+      oidx[gbase + i] = idx[i];
+    }
+  }
+}
+
+// One merge pass: runs of `width` become runs of 2 width. Each thread emits
+// up to 8 consecutive outputs after a merge-path binary search.
+__global__ __launch_bounds__(256) void k_merge_pass(
+    const uint64_t* __restrict__ ikey, const int32_t* __restrict__ iidx,
+    uint64_t* __restrict__ okey, int32_t* __restrict__ oidx,
+    int32_t* __restrict__ out, int n_seg, int seglen, int width) {
+  const long long tpos = (long long)blockIdx.x * 256 + threadIdx.x;
+  const int per_seg = (seglen + 7) / 8;
+  if (tpos >= (long long)n_seg * per_seg) return;
+  const int seg = (int)(tpos / per_seg);
+  const int o = (int)(tpos % per_seg) * 8;
+  const int pair = o / (2 * width);
+  const int a0 = pair * 2 * width;
+  const int a1 = min(a0 + width, seglen);
+  const int b1 = min(a0 + 2 * width, seglen);
+  const int la = a1 - a0, lb = b1 - a1;
+  const int x = o - a0;  // outputs of this pair before ours
+  const size_t base = (size_t)seg * seglen;
+  const uint64_t* KA = ikey + base + a0;
+  const int32_t* IA = iidx + base + a0;
+  const uint64_t* KB = ikey + base + a1;
+  const int32_t* IB = iidx + base + a1;
+  int lo = max(0, x - lb), hi = min(x, la);
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    // take A[mid] before B[x-1-mid]?
+    if (pair_less(KA[mid], IA[mid], KB[x - 1 - mid], IB[x - 1 - mid]))
+      lo = mid + 1;
+    else
+      hi = mid;
+  }
+  int i = lo, j = x - lo;
+  const int n_out = min(8, la + lb - x);
+  for (int e = 0; e < n_out; ++e) {
+    bool take_a;
+    if (i >= la) take_a = false;
+    else if (j >= lb) take_a = true;
+    else take_a = pair_less(KA[i], IA[i], KB[j], IB[j]);
+    const uint64_t kv = take_a ? KA[i] : KB[j];
+    const int32_t iv = take_a ? IA[i] : IB[j];
+    if (take_a) ++i; else ++j;
+    const size_t dst = base + o + e;
+    if (out != nullptr) {
+      out[dst] = iv;
+    } else {
+      okey[dst] = kv;
+      oidx[dst] = iv;
+    }
+  }
+}
+
+__global__ void k_iota(int32_t* __restrict__ out, size_t n, int rowlen) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (size_t)gridDim.x * blockDim.x)
+    out[i] = (int32_t)(i % (size_t)rowlen);
+}
+
+// --------------------------------------------------------------------------
+// Causal restriction: L_t = pi_K without keys >= t S, order kept, t >= 1.
+// cnt[bg, ch, t] = #{entries of chunk ch with segment < t};
+// cum[bg, ch, t] = sum of cnt over earlier chunks (the write offset).
+// --------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_restrict_count(
+    const int32_t* __restrict__ pi_k, int32_t* __restrict__ cnt, int N, int S,
+    int T, int nrc) {
+  extern __shared__ int32_t hist[];  // T + 1 entries
+  const int bg = blockIdx.x / nrc, ch = blockIdx.x % nrc;
+  for (int i = threadIdx.x; i <= T; i += 256) hist[i] = 0;
+  __syncthreads();
+  const int start = ch * kRestrictChunk;
+  const int n = min(kRestrictChunk, N - start);
+  const int32_t* p = pi_k + (size_t)bg * N + start;
+  for (int i = threadIdx.x; i < n; i += 256)
+    atomicAdd(&hist[min(max(p[i] / S, 0), T - 1)], 1);
+  __syncthreads();
+  if (threadIdx.x == 0) {  // exclusive prefix over segments, T <= 2048
+    int run = 0;
+    for (int s = 0; s < T; ++s) {
+      const int v = hist[s];
+      hist[s] = run;
+      run += v;
+    }
+  }
+  __syncthreads();
+  for (int t = threadIdx.x; t < T; t += 256)
+    cnt[((size_t)bg * nrc + ch) * T + t] = hist[t];
+}
+
+__global__ __launch_bounds__(256) void k_restrict_scan(
+    const int32_t* __restrict__ cnt, int32_t* __restrict__ cum, int T,
+    int nrc) {
+  const int bg = blockIdx.x;
+  for (int t = threadIdx.x; t < T; t += 256) {
+    int run = 0;
+    for (int ch = 0; ch < nrc; ++ch) {
+      const size_t i = ((size_t)bg * nrc + ch) * T + t;
+      cum[i] = run;
+      run += cnt[i];
+    }
+  }
+}
+
+// Exclusive scan of one int per thread over a 256-thread workgroup.
+__device__ __forceinline__ int block_exclusive_scan(int v, int* wsum,
+                                                    int& total) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) wsum[wid] = x;
+  __syncthreads();
+  int before = 0;
+  for (int w = 0; w < wid; ++w) before += wsum[w];
+  total = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+  __syncthreads();
+  return before + x - v;
+}
+
+__global__ __launch_bounds__(256) void k_restrict_write(
+    const int32_t* __restrict__ pi_k, const int32_t* __restrict__ cum,
+    int32_t* __restrict__ L, int N, int S, int T, int nrc,
+    long long list_len) {
+  __shared__ int wsum[4];
+  const int bg = blockIdx.x / nrc, ch = blockIdx.x % nrc;
+  const int start = ch * kRestrictChunk;
+  const int n = min(kRestrictChunk, N - start);
+  constexpr int kPer = kRestrictChunk / 256;
+  int32_t keyv[kPer];
+  int32_t segv[kPer];
+  const int32_t* p = pi_k + (size_t)bg * N + start;
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) {
+    const int i = threadIdx.x * kPer + e;
+    keyv[e] = i < n ? p[i] : 0;
+    segv[e] = i < n ? keyv[e] / S : 0x7fffffff;
+  }
+  int32_t* Lbg = L + (size_t)bg * list_len;
+  for (int t = 1; t < T; ++t) {
+    int c = 0;
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) c += segv[e] < t;
+    int total;
+    int pos = block_exclusive_scan(c, wsum, total);
+    pos += cum[((size_t)bg * nrc + ch) * T + t];
+    int32_t* Lt = Lbg + (size_t)S * t * (t - 1) / 2;
+    const int cap = t * S;  // |L_t|; only exceeded if pi_K is no permutation
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) {
+      if (segv[e] < t) {
+        if (pos < cap) Lt[pos] = keyv[e];
+        ++pos;
+      }
+    }
+  }
+}
+
+// --------------------------------------------------------------------------
+// Launchers
+// --------------------------------------------------------------------------
+hipError_t launch_pool_q(const PlanDims& d, const uint16_t* q, int64_t* part,
+                         hipStream_t s) {
+  hipLaunchKernelGGL(k_pool_q, dim3(d.B * d.Hq * d.n_pool_chunks), dim3(256), 0,
+                     s, q, part, d.N, d.n_pool_chunks);
+  return hipGetLastError();
+}
+
+hipError_t launch_pool_reduce(const PlanDims& d, const int64_t* part,
+                              int64_t* pooled, hipStream_t s) {
+  hipLaunchKernelGGL(k_pool_reduce, dim3(d.B * d.Hkv), dim3(kHeadDim), 0, s,
+                     part, pooled, d.Hq, d.Hkv, d.n_pool_chunks);
+  return hipGetLastError();
+}
+
+hipError_t launch_key_score(const PlanDims& d, const uint16_t* k,
+                            const int64_t* pooled, int64_t* vscore,
+                            int32_t* blocksum, hipStream_t s) {
+  hipLaunchKernelGGL(k_key_score, dim3(d.B * d.Hkv * d.n_score_wg), dim3(256),
+                     0, s, k, pooled, vscore, blocksum, d.N, d.n_score_wg);
+  return hipGetLastError();
+}
+
+hipError_t launch_segment_sum(const PlanDims& d, const int32_t* blocksum,
+                              int64_t* segsum, hipStream_t s) {
+  hipLaunchKernelGGL(k_segment_sum, dim3(d.B * d.Hkv * d.T), dim3(kHeadDim), 0,
+                     s, blocksum, segsum, d.N, d.S, d.T);
+  return hipGetLastError();
+}
+
+hipError_t launch_contrast(const PlanDims& d, const uint16_t* k,
+                           const int32_t* L, const int64_t* segsum,
+                           int64_t* contrast, hipStream_t s) {
+  hipLaunchKernelGGL(k_contrast, dim3(d.B * d.Hkv * d.T), dim3(kHeadDim), 0, s,
+                     k, L, segsum, contrast, d.N, d.S, d.T,
+                     (long long)d.list_len);
+  return hipGetLastError();
+}
+
+hipError_t launch_query_score(const PlanDims& d, const uint16_t* q,
+                              const int64_t* contrast, int64_t* u,
+                              hipStream_t s) {
+  hipLaunchKernelGGL(k_query_score, dim3(d.B * d.Hq * d.n_score_wg), dim3(256),
+                     0, s, q, contrast, u, d.Hq, d.Hkv, d.N, d.S, d.T,
+                     d.n_score_wg);
+  return hipGetLastError();
+}
+
+hipError_t launch_segmented_argsort(const int64_t* score, int n_seg,
+                                    int seglen, int rowlen, uint64_t* key_a,
+                                    int32_t* idx_a, uint64_t* key_b,
+                                    int32_t* idx_b, int32_t* out,
+                                    hipStream_t s) {
+  const int chunk = seglen < kSortChunk ? seglen : kSortChunk;
+  const int nch = (seglen + chunk - 1) / chunk;
+  int np2 = 1;
+  while (np2 < chunk) np2 <<= 1;
+  const bool single = nch == 1;
+  hipLaunchKernelGGL(k_chunk_sort, dim3(n_seg * nch), dim3(256), 0, s, score,
+                     seglen, rowlen, chunk, nch, np2, key_a, idx_a,
+                     single ? out : nullptr);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || single) return e;
+  const long long threads = (long long)n_seg * ((seglen + 7) / 8);
+  const int grid = (int)((threads + 255) / 256);
+  uint64_t* ki = key_a; int32_t* ii = idx_a;
+  uint64_t* ko = key_b; int32_t* io = idx_b;
+  for (int width = chunk; width < seglen; width *= 2) {
+    const bool last = 2 * width >= seglen;
+    hipLaunchKernelGGL(k_merge_pass, dim3(grid), dim3(256), 0, s, ki, ii, ko,
+                       io, last ? out : nullptr, n_seg, seglen, width);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    uint64_t* tk = ki; ki = ko; ko = tk;
+    int32_t* ti = ii; ii = io; io = ti;
+  }
+  return hipSuccess;
+}
+
+hipError_t launch_iota(int32_t* out, size_t n, int rowlen, hipStream_t s) {
+  const int grid = (int)((n + 255) / 256 < 65536 ? (n + 255) / 256 : 65536);
+  hipLaunchKernelGGL(k_iota, dim3(grid), dim3(256), 0, s, out, n, rowlen);
+  return hipGetLastError();
+}
+
+hipError_t launch_restrict(const PlanDims& d, const int32_t* pi_k,
+                           int32_t* cnt, int32_t* cum, int32_t* L,
+                           hipStream_t s) {
+  if (d.T < 2) return hipSuccess;
+  const int nbg = d.B * d.Hkv;
+  hipLaunchKernelGGL(k_restrict_count, dim3(nbg * d.n_restrict_chunks),
+                     dim3(256), (d.T + 1) * sizeof(int32_t), s, pi_k, cnt, d.N,
+                     d.S, d.T, d.n_restrict_chunks);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_restrict_scan, dim3(nbg), dim3(256), 0, s, cnt, cum,
+                     d.T, d.n_restrict_chunks);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_restrict_write, dim3(nbg * d.n_restrict_chunks),
+                     dim3(256), 0, s, pi_k, cum, L, d.N, d.S, d.T,
+                     d.n_restrict_chunks, (long long)d.list_len);
+  return hipGetLastError();
+}
+
+}  // namespace sa

@@ -1,0 +1,76 @@
+// Internal host-side launchers of the gfx950 kernels (not part of the ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace sa {
+
+constexpr int kHeadDim = 128;        // supported head dimension
+constexpr int kBlock = 64;           // query-block rows and key-tile keys
+constexpr int kPoolRows = 1024;      // rows per pooling workgroup
+constexpr int kScoreRows = 256;      // rows per scoring workgroup
+constexpr int kSortChunk = 4096;     // elements sorted in LDS by one workgroup
+constexpr int kRestrictChunk = 4096; // pi_K entries per restriction workgroup
+
+struct PlanDims {
+  int B, Hq, Hkv, N, S, T, G;
+  int n_pool_chunks;      // ceil(N / kPoolRows)
+  int n_score_wg;         // ceil(N / kScoreRows)
+  int n_restrict_chunks;  // ceil(N / kRestrictChunk)
+  size_t list_len;        // S T (T - 1) / 2 entries of L per (b, g)
+};
+
+// ---- importance estimator
+hipError_t launch_pool_q(const PlanDims& d, const uint16_t* q, int64_t* part,
+                         hipStream_t s);
+hipError_t launch_pool_reduce(const PlanDims& d, const int64_t* part,
+                              int64_t* pooled, hipStream_t s);
+hipError_t launch_key_score(const PlanDims& d, const uint16_t* k,
+                            const int64_t* pooled, int64_t* vscore,
+                            int32_t* blocksum, hipStream_t s);
+hipError_t launch_segment_sum(const PlanDims& d, const int32_t* blocksum,
+                              int64_t* segsum, hipStream_t s);
+hipError_t launch_contrast(const PlanDims& d, const uint16_t* k,
+                           const int32_t* L, const int64_t* segsum,
+                           int64_t* contrast, hipStream_t s);
+hipError_t launch_query_score(const PlanDims& d, const uint16_t* q,
+                              const int64_t* contrast, int64_t* u,
+                              hipStream_t s);
+
+// ---- index builder
+// Sorts every segment of `seglen` consecutive scores (n_seg segments) by
+// (score descending, index ascending) and writes, for each sorted position,
+// the element's index within its row of `rowlen` elements to `out`.
+hipError_t launch_segmented_argsort(const int64_t* score, int n_seg,
+                                    int seglen, int rowlen, uint64_t* key_a,
+                                    int32_t* idx_a, uint64_t* key_b,
+                                    int32_t* idx_b, int32_t* out,
+                                    hipStream_t s);
+hipError_t launch_iota(int32_t* out, size_t n, int rowlen, hipStream_t s);
+hipError_t launch_restrict(const PlanDims& d, const int32_t* pi_k,
+                           int32_t* cnt, int32_t* cum, int32_t* L,
+                           hipStream_t s);
+
+// ---- attention
+struct AttnArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* o;
+  float* lse;
+  const int32_t* pi_q;
+  const int32_t* L;
+  int32_t* n_out;
+  long long list_len;
+  int B, Hq, Hkv, N, S, T, G;
+  int wg_per_group;
+  int n_groups;
+  double tau;
+  double kappa;
+  float c2;  // kappa * log2(e)
+};
+hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
+
+}  // namespace sa

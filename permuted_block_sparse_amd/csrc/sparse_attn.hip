@@ -1,0 +1,324 @@
+// Host side of libsparse_attn: argument validation, workspace layout and the
+// launch sequence behind the C ABI declared in include/sparse_attn.h.
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+
+#include "sa_launch.h"
+#include "sparse_attn.h"
+
+using namespace sa;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// Offsets of every array inside the caller's workspace.
+struct Layout {
+  size_t pool_part, pooled, vscore, blocksum, segsum, contrast, u;
+  size_t key_a, idx_a, key_b, idx_b;
+  size_t pi_k, L, pi_q, n_I, rcnt, rcum;
+  size_t total;
+};
+
+int validate(const sa_params* p) {
+  if (p == nullptr) return SA_ERR_NULL_POINTER;
+  if (p->batch <= 0 || p->heads_q <= 0 || p->heads_kv <= 0 ||
+      p->seq_len <= 0 || p->head_dim <= 0 || p->segment <= 0 || p->block <= 0)
+    return SA_ERR_UNSUPPORTED_SHAPE;
+  if (p->block != kBlock || p->head_dim != kHeadDim)
+    return SA_ERR_UNSUPPORTED_SHAPE;
+  if (p->segment % kBlock != 0 || p->seq_len % p->segment != 0)
+    return SA_ERR_UNSUPPORTED_SHAPE;
+  if (p->seq_len > (1 << 17)) return SA_ERR_UNSUPPORTED_SHAPE;
+  if (p->heads_q % p->heads_kv != 0 || p->heads_q / p->heads_kv > 256)
+    return SA_ERR_UNSUPPORTED_SHAPE;
+  // every (b, h) row of Q and every sorted segment must index with int32
+  if ((long long)p->batch * p->heads_q * p->seq_len > (1ll << 31) / 2)
+    return SA_ERR_UNSUPPORTED_SHAPE;
+  if (!(p->tau >= 0.0) || std::isinf(p->tau)) return SA_ERR_INVALID_ARG;
+  if (p->flags & ~(SA_NO_QPERM | SA_NO_KVPERM | SA_NO_EARLYSTOP))
+    return SA_ERR_INVALID_ARG;
+  return SA_OK;
+}
+
+PlanDims dims_of(const sa_params* p) {
+  PlanDims d;
+  d.B = p->batch;
+  d.Hq = p->heads_q;
+  d.Hkv = p->heads_kv;
+  d.N = p->seq_len;
+  d.S = p->segment;
+  d.T = p->seq_len / p->segment;
+  d.G = p->heads_q / p->heads_kv;
+  d.n_pool_chunks = (d.N + kPoolRows - 1) / kPoolRows;
+  d.n_score_wg = (d.N + kScoreRows - 1) / kScoreRows;
+  d.n_restrict_chunks = (d.N + kRestrictChunk - 1) / kRestrictChunk;
+  d.list_len = (size_t)d.S * d.T * (d.T - 1) / 2;
+  return d;
+}
+
+Layout layout_of(const PlanDims& d) {
+  Layout L;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align_up(off + bytes);
+    return o;
+  };
+  const size_t nbg = (size_t)d.B * d.Hkv, nbh = (size_t)d.B * d.Hq;
+  const size_t nsort = nbh * d.N;  // >= nbg * N
+  L.pool_part = take(nbh * d.n_pool_chunks * kHeadDim * sizeof(int64_t));
+  L.pooled = take(nbg * kHeadDim * sizeof(int64_t));
+  L.vscore = take(nbg * d.N * sizeof(int64_t));
+  L.blocksum = take(nbg * (d.N / kBlock) * kHeadDim * sizeof(int32_t));
+  L.segsum = take(nbg * d.T * kHeadDim * sizeof(int64_t));
+  L.contrast = take(nbg * d.T * kHeadDim * sizeof(int64_t));
+  L.u = take(nbh * d.N * sizeof(int64_t));
+  L.key_a = take(nsort * sizeof(uint64_t));
+  L.idx_a = take(nsort * sizeof(int32_t));
+  L.key_b = take(nsort * sizeof(uint64_t));
+  L.idx_b = take(nsort * sizeof(int32_t));
+  L.pi_k = take(nbg * d.N * sizeof(int32_t));
+  L.L = take(nbg * (d.list_len > 0 ? d.list_len : 1) * sizeof(int32_t));
+  L.pi_q = take(nbh * d.N * sizeof(int32_t));
+  L.n_I = take(nbh * (d.N / kBlock) * sizeof(int32_t));
+  L.rcnt = take(nbg * d.n_restrict_chunks * d.T * sizeof(int32_t));
+  L.rcum = take(nbg * d.n_restrict_chunks * d.T * sizeof(int32_t));
+  L.total = off;
+  return L;
+}
+
+}  // namespace
+
+struct sa_plan {
+  sa_params p;
+  PlanDims d;
+  Layout lay;
+  char* ws;
+  const void* q;
+  const void* k;
+
+  template <class T>
+  T* at(size_t off) const {
+    return reinterpret_cast<T*>(ws + off);
+  }
+};
+
+namespace {
+
+int hip_status(hipError_t e) { return e == hipSuccess ? SA_OK : SA_ERR_HIP; }
+
+// Everything that depends on the global KV order: restricted lists,
+// contrast vectors, query scores and the query order.
+int build_from_kv_order(sa_plan* pl, hipStream_t s) {
+  const PlanDims& d = pl->d;
+  hipError_t e;
+  e = launch_restrict(d, pl->at<int32_t>(pl->lay.pi_k),
+                      pl->at<int32_t>(pl->lay.rcnt),
+                      pl->at<int32_t>(pl->lay.rcum), pl->at<int32_t>(pl->lay.L),
+                      s);
+  if (e != hipSuccess) return SA_ERR_HIP;
+  e = launch_contrast(d, static_cast<const uint16_t*>(pl->k),
+                      pl->at<int32_t>(pl->lay.L),
+                      pl->at<int64_t>(pl->lay.segsum),
+                      pl->at<int64_t>(pl->lay.contrast), s);
+  if (e != hipSuccess) return SA_ERR_HIP;
+  e = launch_query_score(d, static_cast<const uint16_t*>(pl->q),
+                         pl->at<int64_t>(pl->lay.contrast),
+                         pl->at<int64_t>(pl->lay.u), s);
+  if (e != hipSuccess) return SA_ERR_HIP;
+  const size_t nbh = (size_t)d.B * d.Hq;
+  if (pl->p.flags & SA_NO_QPERM) {
+    e = launch_iota(pl->at<int32_t>(pl->lay.pi_q), nbh * d.N, d.N, s);
+  } else {
+    e = launch_segmented_argsort(
+        pl->at<int64_t>(pl->lay.u), (int)(nbh * d.T), d.S, d.N,
+        pl->at<uint64_t>(pl->lay.key_a), pl->at<int32_t>(pl->lay.idx_a),
+        pl->at<uint64_t>(pl->lay.key_b), pl->at<int32_t>(pl->lay.idx_b),
+        pl->at<int32_t>(pl->lay.pi_q), s);
+  }
+  return hip_status(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t sparse_attn_workspace_bytes(const sa_params* p) {
+  if (validate(p) != SA_OK) return 0;
+  return layout_of(dims_of(p)).total;
+}
+
+int sparse_attn_plan(const sa_params* p, const void* q, const void* k,
+                     void* workspace, size_t workspace_bytes,
+                     hipStream_t stream, sa_plan** out) {
+  if (out == nullptr) return SA_ERR_NULL_POINTER;
+  *out = nullptr;
+  const int st = validate(p);
+  if (st != SA_OK) return st;
+  if (q == nullptr || k == nullptr || workspace == nullptr)
+    return SA_ERR_NULL_POINTER;
+  if (reinterpret_cast<uintptr_t>(workspace) % kAlign != 0)
+    return SA_ERR_INVALID_ARG;
+  const PlanDims d = dims_of(p);
+  const Layout lay = layout_of(d);
+  if (workspace_bytes < lay.total) return SA_ERR_WORKSPACE_TOO_SMALL;
+
+  sa_plan* pl = new (std::nothrow) sa_plan;
+  if (pl == nullptr) return SA_ERR_HOST_ALLOC;
+  pl->p = *p;
+  pl->d = d;
+  pl->lay = lay;
+  pl->ws = static_cast<char*>(workspace);
+  pl->q = q;
+  pl->k = k;
+
+  const uint16_t* qb = static_cast<const uint16_t*>(q);
+  const uint16_t* kb = static_cast<const uint16_t*>(k);
+  hipError_t e = launch_pool_q(d, qb, pl->at<int64_t>(lay.pool_part), stream);
+  if (e == hipSuccess)
+    e = launch_pool_reduce(d, pl->at<int64_t>(lay.pool_part),
+                           pl->at<int64_t>(lay.pooled), stream);
+  if (e == hipSuccess)
+    e = launch_key_score(d, kb, pl->at<int64_t>(lay.pooled),
+                         pl->at<int64_t>(lay.vscore),
+                         pl->at<int32_t>(lay.blocksum), stream);
+  if (e == hipSuccess)
+    e = launch_segment_sum(d, pl->at<int32_t>(lay.blocksum),
+                           pl->at<int64_t>(lay.segsum), stream);
+  if (e == hipSuccess) {
+    const size_t nbg = (size_t)d.B * d.Hkv;
+    if (p->flags & SA_NO_KVPERM)
+      e = launch_iota(pl->at<int32_t>(lay.pi_k), nbg * d.N, d.N, stream);
+    else
+      e = launch_segmented_argsort(
+          pl->at<int64_t>(lay.vscore), (int)nbg, d.N, d.N,
+          pl->at<uint64_t>(lay.key_a), pl->at<int32_t>(lay.idx_a),
+          pl->at<uint64_t>(lay.key_b), pl->at<int32_t>(lay.idx_b),
+          pl->at<int32_t>(lay.pi_k), stream);
+  }
+  int rc = hip_status(e);
+  if (rc == SA_OK) rc = build_from_kv_order(pl, stream);
+  if (rc != SA_OK) {
+    delete pl;
+    return rc;
+  }
+  *out = pl;
+  return SA_OK;
+}
+
+int sparse_attn_prefill(const sa_plan* plan, const void* q, const void* k,
+                        const void* v, void* o, float* lse,
+                        hipStream_t stream) {
+  if (plan == nullptr || q == nullptr || k == nullptr || v == nullptr ||
+      o == nullptr)
+    return SA_ERR_NULL_POINTER;
+  const PlanDims& d = plan->d;
+  AttnArgs a;
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.o = static_cast<uint16_t*>(o);
+  a.lse = lse;
+  a.pi_q = plan->at<int32_t>(plan->lay.pi_q);
+  a.L = plan->at<int32_t>(plan->lay.L);
+  a.n_out = plan->at<int32_t>(plan->lay.n_I);
+  a.list_len = (long long)d.list_len;
+  a.B = d.B;
+  a.Hq = d.Hq;
+  a.Hkv = d.Hkv;
+  a.N = d.N;
+  a.S = d.S;
+  a.T = d.T;
+  a.G = d.G;
+  const int qblocks = d.G * (d.S / kBlock);
+  a.wg_per_group = (qblocks + 3) / 4;
+  a.n_groups = d.B * d.Hkv * d.T;
+  a.tau = (plan->p.flags & SA_NO_EARLYSTOP) ? 0.0 : plan->p.tau;
+  a.kappa = 1.0 / std::sqrt((double)kHeadDim);
+  a.c2 = (float)(a.kappa * 1.4426950408889634074);
+  return hip_status(launch_attention(a, stream));
+}
+
+int sparse_attn_plan_set_tau(sa_plan* plan, double tau) {
+  if (plan == nullptr) return SA_ERR_NULL_POINTER;
+  if (!(tau >= 0.0) || std::isinf(tau)) return SA_ERR_INVALID_ARG;
+  plan->p.tau = tau;
+  return SA_OK;
+}
+
+size_t sparse_attn_plan_export_bytes(const sa_plan* plan, int what) {
+  if (plan == nullptr) return 0;
+  const PlanDims& d = plan->d;
+  const size_t nbg = (size_t)d.B * d.Hkv, nbh = (size_t)d.B * d.Hq;
+  switch (what) {
+    case SA_EXPORT_PI_K: return nbg * d.N * sizeof(int32_t);
+    case SA_EXPORT_PI_Q: return nbh * d.N * sizeof(int32_t);
+    case SA_EXPORT_L: return nbg * d.list_len * sizeof(int32_t);
+    case SA_EXPORT_N_I: return nbh * (d.N / kBlock) * sizeof(int32_t);
+    case SA_EXPORT_KEY_SCORE: return nbg * d.N * sizeof(int64_t);
+    case SA_EXPORT_QUERY_SCORE: return nbh * d.N * sizeof(int64_t);
+    case SA_EXPORT_CONTRAST: return nbg * d.T * kHeadDim * sizeof(int64_t);
+    case SA_EXPORT_POOLED: return nbg * kHeadDim * sizeof(int64_t);
+    default: return 0;
+  }
+}
+
+int sparse_attn_plan_export(const sa_plan* plan, int what, void* host_dst,
+                            size_t bytes, hipStream_t stream) {
+  if (plan == nullptr || host_dst == nullptr) return SA_ERR_NULL_POINTER;
+  const size_t need = sparse_attn_plan_export_bytes(plan, what);
+  if (need == 0 && what != SA_EXPORT_L) return SA_ERR_INVALID_ARG;
+  if (bytes < need) return SA_ERR_WORKSPACE_TOO_SMALL;
+  if (need == 0) return SA_OK;
+  size_t off = 0;
+  switch (what) {
+    case SA_EXPORT_PI_K: off = plan->lay.pi_k; break;
+    case SA_EXPORT_PI_Q: off = plan->lay.pi_q; break;
+    case SA_EXPORT_L: off = plan->lay.L; break;
+    case SA_EXPORT_N_I: off = plan->lay.n_I; break;
+    case SA_EXPORT_KEY_SCORE: off = plan->lay.vscore; break;
+    case SA_EXPORT_QUERY_SCORE: off = plan->lay.u; break;
+    case SA_EXPORT_CONTRAST: off = plan->lay.contrast; break;
+    case SA_EXPORT_POOLED: off = plan->lay.pooled; break;
+  }
+  hipError_t e = hipMemcpyAsync(host_dst, plan->ws + off, need,
+                                hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  return hip_status(e);
+}
+
+int sparse_attn_plan_set_kv_order(sa_plan* plan, const void* pi_k,
+                                  hipStream_t stream) {
+  if (plan == nullptr || pi_k == nullptr) return SA_ERR_NULL_POINTER;
+  const size_t bytes = (size_t)plan->d.B * plan->d.Hkv * plan->d.N *
+                       sizeof(int32_t);
+  hipError_t e = hipMemcpyAsync(plan->ws + plan->lay.pi_k, pi_k, bytes,
+                                hipMemcpyDeviceToDevice, stream);
+  if (e != hipSuccess) return SA_ERR_HIP;
+  return build_from_kv_order(plan, stream);
+}
+
+void sparse_attn_plan_destroy(sa_plan* plan) { delete plan; }
+
+const char* sparse_attn_status_string(int status) {
+  switch (status) {
+    case SA_OK: return "ok";
+    case SA_ERR_INVALID_ARG: return "invalid argument";
+    case SA_ERR_UNSUPPORTED_SHAPE: return "unsupported shape";
+    case SA_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case SA_ERR_HIP: return "HIP runtime error";
+    case SA_ERR_NULL_POINTER: return "null pointer";
+    case SA_ERR_HOST_ALLOC: return "host allocation failed";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

@@ -312,16 +312,13 @@ def check_strict_stop(O):
     first local block, so E_diag = 64 and p_k = 64 / (64 + 64 (k + 1)) =
     1 / (k + 2): with tau = 1/4, p_2 = tau is visited and k = 3 stops."""
     S, d = 128, 16
-    k64 = np.zeros((2 * S, d))
-    rows = np.full(64, S + 63)
-    Lt = np.arange(S)
-    n, ps = O.block_stop(np.ones(d), rows, 1, k64, Lt, S, 0.25,
-                         1.0 / math.sqrt(d))
+    kap = 1.0 / math.sqrt(d)
+    local = np.zeros((S // 64, d))
+    n, ps = O.block_stop(np.ones(d), np.full(64, S + 63), 1, local,
+                         np.zeros((2, d)), S, 0.25, kap)
     assert n == 2 and list(ps) == [0.5, 1 / 3]   # only 2 tiles exist
-    Lt = np.arange(2 * S)
-    k64 = np.zeros((3 * S, d))
-    n, ps = O.block_stop(np.ones(d), np.full(64, 2 * S + 63), 2, k64, Lt,
-                         S, 0.25, 1.0 / math.sqrt(d))
+    n, ps = O.block_stop(np.ones(d), np.full(64, 2 * S + 63), 2, local,
+                         np.zeros((4, d)), S, 0.25, kap)
     assert n == 3 and list(ps) == [0.5, 1 / 3, 0.25, 0.2]
 
 

@@ -1,0 +1,144 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Indices and integer scores must match bit for bit; stop points must match
+except on documented near-tau ties; outputs must be within 2e-2 max-abs and
+1e-4 MSE of the float64 oracle evaluated on the same stop points.
+"""
+import numpy as np
+import pytest
+
+import oracle as O
+from synthetic import StripeSpec, get_config, make_stripe_inputs
+from tests.gpu_helpers import (assert_outputs_close, assert_plan_equal,
+                               run_gpu, say, stop_mismatches)
+
+pytestmark = pytest.mark.gpu
+
+
+def _spec(B, Hq, Hkv, N, seed, n_vert=16, n_horiz=8, window=64):
+    return StripeSpec(B, Hq, Hkv, N, 128, n_vert=n_vert, n_horiz=n_horiz,
+                      window=window, seed=seed)
+
+
+CASES = [
+    # name, spec, segment, taus, flags
+    ("tiny_n2048_s512", get_config(1).spec, 512, (0.005, 0.05, 0.2), 0),
+    ("gqa_b2_h4_kv2_n1024", _spec(2, 4, 2, 1024, 21), 256, (0.0, 0.02, 0.1),
+     0),
+    ("ragged_n640_s128", _spec(1, 2, 1, 640, 22), 128, (0.05, 0.3), 0),
+    ("s64_one_block_per_segment", _spec(1, 2, 2, 768, 23), 64, (0.1, 0.4), 0),
+    ("g8_h8_kv1_n512", _spec(1, 8, 1, 512, 24), 128, (0.03,), 0),
+    ("single_segment_n256", _spec(1, 2, 1, 256, 25), 256, (0.5,), 0),
+    ("single_block_n64", _spec(1, 1, 1, 64, 26, n_vert=2, n_horiz=1,
+                               window=16), 64, (0.1,), 0),
+    ("no_qperm", _spec(1, 4, 1, 1024, 27), 256, (0.05,), O.SA_NO_QPERM),
+    ("no_kvperm", _spec(1, 4, 1, 1024, 28), 256, (0.05,), O.SA_NO_KVPERM),
+    ("no_earlystop", _spec(1, 2, 1, 1024, 29), 256, (0.2,), O.SA_NO_EARLYSTOP),
+    ("s4096_merge_sort_n8192", _spec(1, 2, 1, 8192, 30, n_vert=64,
+                                     window=128), 4096, (0.02,), 0),
+]
+
+
+def _check_case(q, k, v, S, tau, flags):
+    pl = O.plan(q, k, S, flags=flags)
+    n_orc, traces = O.stop_points(q, k, pl, tau)
+    g = run_gpu(q, k, v, S, tau, flags)
+    assert_plan_equal(g, pl)
+    ties = stop_mismatches(g["n_I"], n_orc, traces,
+                           0.0 if flags & O.SA_NO_EARLYSTOP else tau)
+    n_use = n_orc.copy()
+    for b, h, I in ties:
+        n_use[b, h, I] = g["n_I"][b, h, I]
+    o_ref, lse_ref = O.attend(q, k, v, pl, n_use)
+    err, mse = assert_outputs_close(g["o"], o_ref, g["lse"], lse_ref)
+    return err, mse, len(ties), g, pl, n_orc
+
+
+@pytest.mark.parametrize("name,spec,S,taus,flags", CASES,
+                         ids=[c[0] for c in CASES])
+def test_parity_small(name, spec, S, taus, flags):
+    q, k, v = make_stripe_inputs(spec)
+    for tau in taus:
+        say(f"[parity] {name} tau={tau} flags={flags}")
+        err, mse, nties, g, pl, n_orc = _check_case(q, k, v, S, tau, flags)
+        say(f"   max_abs={err:.3g} mse={mse:.3g} ties={nties} "
+            f"mean_n_I={g['n_I'].mean():.2f}")
+
+
+def test_tau0_is_dense_and_kv_order_invariant():
+    spec = _spec(1, 4, 2, 1024, 31)
+    q, k, v = make_stripe_inputs(spec)
+    od, ld = O.dense_causal(q, k, v)
+    say("[parity] tau=0 vs dense")
+    g = run_gpu(q, k, v, 256, 0.0)
+    assert_outputs_close(g["o"], od, g["lse"], ld)
+    perm = np.stack([np.random.default_rng(5 + i).permutation(1024)
+                     for i in range(2)])[None]
+    say("[parity] tau=0 with an injected KV order vs dense")
+    g2 = run_gpu(q, k, v, 256, 0.0, kv_order=perm)
+    assert np.array_equal(g2["pi_k"], perm)
+    pl = O.plan(q, k, 256, kv_order=perm)
+    assert np.array_equal(g2["L"], pl.L)
+    assert np.array_equal(g2["pi_q"], pl.pi_q)
+    assert_outputs_close(g2["o"], od, g2["lse"], ld)
+
+
+def test_deterministic():
+    spec = _spec(1, 4, 1, 2048, 32)
+    q, k, v = make_stripe_inputs(spec)
+    say("[parity] determinism")
+    a = run_gpu(q, k, v, 512, 0.02)
+    b = run_gpu(q, k, v, 512, 0.02)
+    for key in ("o", "lse", "pi_k", "pi_q", "L", "n_I"):
+        assert np.array_equal(a[key], b[key]), key
+
+
+def test_causal_values_and_later_segments():
+    spec = _spec(1, 2, 1, 1024, 33)
+    q, k, v = make_stripe_inputs(spec)
+    say("[parity] causality")
+    base = run_gpu(q, k, v, 256, 0.05)
+    i = 600
+    rng = np.random.default_rng(0)
+    v2 = v.copy()
+    v2[:, :, i + 1:] = rng.integers(0x3c00, 0x4000, size=v2[:, :, i + 1:].shape,
+                                    dtype=np.uint16)
+    pert = run_gpu(q, k, v2, 256, 0.05)
+    assert np.array_equal(base["o"][:, :, :i + 1], pert["o"][:, :, :i + 1])
+    assert not np.array_equal(base["o"][:, :, i + 1:], pert["o"][:, :, i + 1:])
+    # keys of later segments change nothing in earlier segments
+    k2 = k.copy()
+    k2[:, :, 768:] = rng.integers(0x3c00, 0x4000, size=k2[:, :, 768:].shape,
+                                  dtype=np.uint16)
+    pert = run_gpu(q, k2, v, 256, 0.05)
+    assert np.array_equal(base["o"][:, :, :768], pert["o"][:, :, :768])
+    assert np.array_equal(base["n_I"][:, :, :12], pert["n_I"][:, :, :12])
+
+
+def test_parity_llama_layer_n32k_full_plan_sampled_outputs():
+    """Llama-3.1-8B-shaped layer at N = 32768 (the 32K workload): every index
+    array and every stop point against the oracle; outputs on 48 sampled
+    query blocks (oracle row by row)."""
+    cfg = get_config(2)
+    q, k, v = make_stripe_inputs(cfg.spec)
+    S, tau = cfg.segment, cfg.tau
+    say("[parity] 32K workload: oracle plan")
+    pl = O.plan(q, k, S)
+    say("[parity] 32K workload: GPU")
+    g = run_gpu(q, k, v, S, tau)
+    assert_plan_equal(g, pl)
+    say("[parity] 32K workload: oracle stop points (all blocks)")
+    n_orc, traces = O.stop_points(q, k, pl, tau)
+    ties = stop_mismatches(g["n_I"], n_orc, traces, tau)
+    say(f"   ties={len(ties)} mean_n_I={g['n_I'].mean():.2f}")
+    rng = np.random.default_rng(7)
+    nb = q.shape[2] // 64
+    blocks = [(0, int(h), int(I)) for h, I in zip(
+        rng.integers(0, 32, 48), rng.integers(0, nb, 48))]
+    blocks += [(0, 31, nb - 1), (0, 0, 0), (0, 5, nb // 2)]
+    n_use = n_orc.copy()
+    for b, h, I in ties:
+        n_use[b, h, I] = g["n_I"][b, h, I]
+    o_ref, lse_ref = O.attend(q, k, v, pl, n_use, blocks=blocks)
+    err, mse = assert_outputs_close(g["o"], o_ref, g["lse"], lse_ref)
+    say(f"   sampled blocks: max_abs={err:.3g} mse={mse:.3g}")

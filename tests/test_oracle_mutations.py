@@ -32,11 +32,13 @@ MUTANTS = [
      "Lt = order[order <= t * S][:t * S]"),
     ("stop_le", "if p < tau:", "if p <= tau:"),
     ("diag_weight", "acc += (nv / BLOCK) * math.exp", "acc += nv * math.exp"),
-    ("tile_mass_1", "E = BLOCK * np.exp(kap * (kbar @ qbar))",
-     "E = np.exp(kap * (kbar @ qbar))"),
+    ("tile_mass_1", "E = BLOCK * np.exp(kap * (tile_means @ qbar))",
+     "E = np.exp(kap * (tile_means @ qbar))"),
     ("no_running_sum", "        acc += E[kk]\n", "\n"),
-    ("estimate_no_kappa", "E = BLOCK * np.exp(kap * (kbar @ qbar))",
-     "E = BLOCK * np.exp(kbar @ qbar)"),
+    ("estimate_no_kappa", "E = BLOCK * np.exp(kap * (tile_means @ qbar))",
+     "E = BLOCK * np.exp(tile_means @ qbar)"),
+    ("local_means_shifted", "local_means = block_means(k64, np.arange(t * S, (t + 1) * S))",
+     "local_means = block_means(k64, np.arange(t * S - S, t * S))"),
     ("ratio_without_self", "p = E[kk] / (acc + E[kk])", "p = E[kk] / acc"),
     ("qbar_natural_rows", "qbar = q64[rows].mean(axis=0)",
      "qbar = q64[I * BLOCK:(I + 1) * BLOCK].mean(axis=0)"),

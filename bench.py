@@ -1,0 +1,339 @@
+#!/usr/bin/env python3
+"""Benchmark: permuted early-stopping block-sparse prefill attention, 128K.
+
+One step = the whole hot path on one attention layer of the Llama-3.1-8B
+shape at N = 131072 (32 query heads, 8 KV heads, d = 128, bf16, causal):
+sparse_attn_plan (pooling, scores, both orders, restricted lists) followed by
+sparse_attn_prefill (gather attention with the tau stop and the scatter),
+inputs resident in HBM. Prints ONE JSON line (rank 0, one GPU).
+
+Besides the timed steps the run reports: the stop statistics (pair sparsity,
+visited tiles), MSE against dense attention (the same kernel at tau = 0,
+itself checked against the float64 oracle on sampled rows), the tau sweep of
+the workload, planner overhead, the attention kernel's MFMA roofline, and
+the CPU oracle timed on the host's cores on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+BF16_PEAK_TFLOPS = 2500.0     # MI355X dense bf16 MFMA (no sparsity)
+HBM_PEAK_GBS = 8000.0
+TILE_FLOP = 4 * 64 * 64 * 128  # QK^T + PV of one 64 x 64 tile, d = 128
+METRIC = "ms/layer sparse prefill attn @128K; sparsity & MSE; MFMA util vs bf16 peak"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_traffic_n128k.json")
+ATTN_SOURCE = os.path.join(ROOT, "permuted_block_sparse_amd", "csrc",
+                           "attn_kernel.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--config", type=int, default=3,
+                    help="workload id (3 = Llama-3.1-8B layer at 128K)")
+    ap.add_argument("--tau", type=float, default=None)
+    ap.add_argument("--segment", type=int, default=None)
+    ap.add_argument("--no-extras", action="store_true",
+                    help="only the timed steps (for profiling runs)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def source_hash(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on exactly one GPU: this build has no multi-GPU "
+              "path (the method shards over independent KV heads with no "
+              "communication; see DESIGN.md). Use --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import permuted_block_sparse_amd as pbs
+    from synthetic import get_config, make_stripe_inputs
+
+    cfg = get_config(args.config)
+    spec = cfg.spec
+    S = args.segment or cfg.segment
+    tau = cfg.tau if args.tau is None else args.tau
+    B, Hq, Hkv, N, d = (spec.batch, spec.heads_q, spec.heads_kv,
+                        spec.seq_len, spec.head_dim)
+    dev = torch.device("cuda:0")
+    log(f"[bench] workload {cfg.name}: generating inputs")
+    t0 = time.time()
+    q, k, v = make_stripe_inputs(spec)
+    log(f"[bench] inputs ready in {time.time() - t0:.1f}s; uploading")
+
+    def up(x):
+        return torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
+
+    tq, tk, tv = up(q), up(k), up(v)
+    stream = torch.cuda.current_stream()
+    out = torch.empty_like(tq)
+
+    def step(t_=tau):
+        pl = pbs.plan(tq, tk, S, t_)
+        pbs.prefill(pl, tq, tk, tv, out=out)
+        return pl
+
+    for i in range(args.warmup):
+        step()
+        torch.cuda.synchronize()
+        log(f"[bench] warmup {i + 1}/{args.warmup} done")
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        pl = step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / args.steps
+    log(f"[bench] timed {args.steps} steps: {ms_step:.3f} ms/step")
+
+    # ---- stage split with HIP events on the launch stream
+    def timed(fn, reps):
+        ts = []
+        for _ in range(reps):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b))
+        return float(np.median(ts)), float(np.mean(ts))
+
+    plan_ms, _ = timed(lambda: pbs.plan(tq, tk, S, tau), max(3, args.steps))
+    pl = pbs.plan(tq, tk, S, tau)
+    attn_med, attn_mean = timed(lambda: pbs.prefill(pl, tq, tk, tv, out=out),
+                                max(3, args.steps))
+    n_I = pl.n_I()
+    pi_q = pl.pi_q()
+    log(f"[bench] plan {plan_ms:.3f} ms, prefill {attn_med:.3f} ms")
+
+    T = N // S
+    nb = N // 64
+    # visited local blocks: c with some row of the block at or after the
+    # block's first key
+    blk_max = pi_q.reshape(B, Hq, nb, 64).max(axis=3)
+    seg_of_blk = (np.arange(nb) * 64) // S
+    diag_tiles = int(((blk_max - seg_of_blk * S) // 64 + 1).sum())
+    sparse_tiles = int(n_I.sum())
+    visited = diag_tiles + sparse_tiles
+    flop_launch = visited * TILE_FLOP
+    achieved = flop_launch / (attn_mean * 1e-3) / 1e12
+    sel_pairs = B * Hq * T * S * (S + 1) / 2 + 4096.0 * sparse_tiles
+    pair_sparsity = 1.0 - sel_pairs / (B * Hq * N * (N + 1) / 2)
+    dense_flop = 4.0 * d * N * (N + 1) / 2 * B * Hq
+
+    result = {
+        "metric": METRIC,
+        "value": round(ms_step, 4),
+        "unit": "ms/layer",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic stripe-structured Q/K/V (seeded), random-init "
+                "stand-in for a Llama-3.1-8B attention layer",
+        "config": {"workload": cfg.name, "batch": B, "heads_q": Hq,
+                   "heads_kv": Hkv, "seq_len": N, "head_dim": d,
+                   "segment": S, "block": 64, "tau": tau,
+                   "parallelism": "single GPU"},
+        "stages_ms": {"plan": round(plan_ms, 4),
+                      "prefill": round(attn_med, 4),
+                      "overhead_frac": round(plan_ms / attn_med, 4)},
+        "stop": {"pair_sparsity": round(pair_sparsity, 5),
+                 "mean_n_I": round(float(n_I.mean()), 2),
+                 "visited_sparse_tiles": sparse_tiles,
+                 "visited_local_tiles": diag_tiles,
+                 "dense_equiv_tflops": round(dense_flop / attn_med / 1e9, 1),
+                 "visited_tile_tflops": round(achieved, 1)},
+    }
+    traffic = None
+    try:
+        with open(TRAFFIC_FILE) as f:
+            tr = json.load(f)
+        if (tr.get("source_sha256_16") == source_hash(ATTN_SOURCE)
+                and tr.get("workload") == cfg.name and tr.get("tau") == tau):
+            traffic = tr.get("hbm_bytes_per_launch")
+    except (OSError, ValueError):
+        pass
+    result["roofline"] = {
+        "bound": "mfma", "achieved": round(achieved, 2),
+        "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+        "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
+        "traffic": traffic, "kernel": "k_attn_fwd",
+        "flop_per_launch": flop_launch,
+        "avg_launch_ms": round(attn_mean, 4)}
+
+    if not args.no_extras:
+        result.update(extras(args, cfg, q, k, v, tq, tk, tv, pl, out, S,
+                             tau, timed))
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(cfg, q, k, v, S, tau,
+                                              nb_total=B * Hq * nb)
+    print(json.dumps(result), flush=True)
+
+
+def extras(args, cfg, q, k, v, tq, tk, tv, pl, out, S, tau, timed):
+    """tau sweep, dense reference, MSE, sampled-row validation."""
+    import torch
+    import permuted_block_sparse_amd as pbs
+    import oracle as O  # only for the sampled-row validation
+
+    def bf16_tensor_to_f64(t):
+        u = t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+        return (u.astype(np.uint32) << np.uint32(16)).view(
+            np.float32).astype(np.float64)
+
+    spec = cfg.spec
+    B, Hq, Hkv, N = spec.batch, spec.heads_q, spec.heads_kv, spec.seq_len
+    T = N // S
+    res = {}
+    # dense reference: the same kernel with tau = 0 visits every tile
+    pl.set_tau(0.0)
+    dense = torch.empty_like(tq)
+    dense_ms, _ = timed(lambda: pbs.prefill(pl, tq, tk, tv, out=dense), 2)
+    log(f"[bench] tau=0 (dense) prefill {dense_ms:.3f} ms")
+    sweep = []
+    taus = sorted(set(cfg.taus) | {tau})
+    for t_ in taus:
+        pl.set_tau(t_)
+        o_t = torch.empty_like(tq)
+        ms, _ = timed(lambda: pbs.prefill(pl, tq, tk, tv, out=o_t), 3)
+        n_I = pl.n_I()
+        sel = B * Hq * T * S * (S + 1) / 2 + 4096.0 * n_I.sum()
+        sp = 1.0 - sel / (B * Hq * N * (N + 1) / 2)
+        diff = (o_t.float() - dense.float())
+        mse = float((diff * diff).mean().item())
+        per_head = (diff * diff).mean(dim=(0, 2, 3)).cpu().numpy()
+        sweep.append({"tau": t_, "prefill_ms": round(ms, 4),
+                      "pair_sparsity": round(float(sp), 5),
+                      "mse_vs_dense": mse,
+                      "mse_per_head_max": float(per_head.max()),
+                      "speedup_vs_dense": round(dense_ms / ms, 3)})
+        log(f"[bench] tau={t_}: {ms:.3f} ms sparsity={sp:.4f} mse={mse:.3g}")
+    pl.set_tau(tau)
+    res["tau_sweep"] = sweep
+    res["dense_prefill_ms"] = round(dense_ms, 4)
+
+    # sampled validation at full size in the timed launch configuration:
+    # KV group 0's plan against the oracle, and sampled blocks' stop points
+    # and outputs (and the dense reference on sampled rows)
+    log("[bench] validating sampled blocks against the oracle")
+    G = Hq // Hkv
+    qs = np.ascontiguousarray(q[:1, :G])
+    ks = np.ascontiguousarray(k[:1, :1])
+    vs = np.ascontiguousarray(v[:1, :1])
+    ref = O.plan(qs, ks, S)
+    ok_plan = (np.array_equal(pl.pi_k()[0, 0], ref.pi_k[0, 0])
+               and np.array_equal(pl.pi_q()[0, :G], ref.pi_q[0])
+               and np.array_equal(pl.restricted_lists()[0, 0], ref.L[0, 0]))
+    rng = np.random.default_rng(0)
+    nb = N // 64
+    blocks = [(0, int(h), int(I)) for h, I in
+              zip(rng.integers(0, G, 8), rng.integers(nb // 8, nb, 8))]
+    blocks.append((0, 0, nb - 1))
+    n_ref, traces = O.stop_points(qs, ks, ref, tau, blocks=blocks)
+    pl.set_tau(tau)
+    pbs.prefill(pl, tq, tk, tv, out=out)
+    n_gpu = pl.n_I()[:1, :G]
+    ties = 0
+    n_use = n_ref.copy()
+    for b, h, I in blocks:
+        if n_gpu[b, h, I] != n_ref[b, h, I]:
+            m = int(min(n_gpu[b, h, I], n_ref[b, h, I]))
+            assert abs(traces[(b, h, I)][m] - tau) <= 1e-4 * tau
+            ties += 1
+            n_use[b, h, I] = n_gpu[b, h, I]
+    o_ref, _ = O.attend(qs, ks, vs, ref, n_use, blocks=blocks)
+    o_gpu = bf16_tensor_to_f64(out[:1, :G])
+    mask = ~np.isnan(o_ref[..., 0])
+    err = float(np.abs(o_gpu[mask] - o_ref[mask]).max())
+    mse_s = float(np.mean((o_gpu[mask] - o_ref[mask]) ** 2))
+    rows = rng.integers(0, N, 16)
+    od, _ = O.dense_causal(qs, ks, vs, rows=rows, heads=[(0, 0)])
+    dg = bf16_tensor_to_f64(dense[:1, :1])
+    derr = float(np.abs(dg[0, 0, rows] - od[0, 0, rows]).max())
+    res["validation"] = {
+        "plan_group0_bit_exact": bool(ok_plan),
+        "sampled_blocks": len(blocks), "stop_ties": ties,
+        "stop_points_equal": bool(all(n_gpu[b, h, I] == n_use[b, h, I]
+                                      for b, h, I in blocks)),
+        "max_abs_err": err, "mse": mse_s,
+        "dense_sampled_rows_max_abs_err": derr,
+        "within_tolerance": bool(err <= 2e-2 and mse_s <= 1e-4
+                                 and derr <= 2e-2 and ok_plan)}
+    log(f"[bench] validation: {res['validation']}")
+    return res
+
+
+def cpu_baseline(cfg, q, k, v, S, tau, nb_total):
+    """The oracle, as it stands, on a bounded sample of the workload: the
+    full plan of one KV group plus stop points and attention of 24 query
+    blocks of that group; extrapolated linearly to the whole layer (plan x
+    number of KV groups, attention x number of query blocks)."""
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()]
+                      or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    spec = cfg.spec
+    G = spec.heads_q // spec.heads_kv
+    qs = np.ascontiguousarray(q[:1, :G])
+    ks = np.ascontiguousarray(k[:1, :1])
+    vs = np.ascontiguousarray(v[:1, :1])
+    log("[bench] cpu baseline: oracle plan of one KV group")
+    t0 = time.perf_counter()
+    ref = O.plan(qs, ks, S)
+    t_plan = time.perf_counter() - t0
+    nb = spec.seq_len // 64
+    rng = np.random.default_rng(1)
+    blocks = [(0, int(h), int(I)) for h, I in
+              zip(rng.integers(0, G, 24), rng.integers(0, nb, 24))]
+    log("[bench] cpu baseline: oracle stop points + attention of 24 blocks")
+    t0 = time.perf_counter()
+    n_I, _ = O.stop_points(qs, ks, ref, tau, blocks=blocks)
+    O.attend(qs, ks, vs, ref, n_I, blocks=blocks)
+    t_blk = (time.perf_counter() - t0) / len(blocks)
+    groups = spec.batch * spec.heads_kv
+    est_s = t_plan * groups + t_blk * nb_total
+    return {"value": round(est_s * 1e3, 1), "unit": "ms/layer",
+            "cores": int(threads), "kind": "oracle",
+            "sample": f"oracle plan of 1 of {groups} KV groups "
+                      f"({t_plan:.2f} s) + stop points and attention of 24 "
+                      f"of {nb_total} query blocks ({t_blk * 1e3:.1f} ms "
+                      f"each), extrapolated linearly to the layer",
+            "extrapolated": True}
+
+
+if __name__ == "__main__":
+    main()

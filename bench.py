@@ -52,6 +52,12 @@ def parse():
     ap.add_argument("--no-extras", action="store_true",
                     help="only the timed steps (for profiling runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--profile-once", action="store_true",
+                    help="one plan + one prefill, no timing (counter runs)")
+    ap.add_argument("--copy-calibration", type=int, default=0,
+                    metavar="MIB",
+                    help="only copy MIB MiB device->device (a plain copy "
+                         "kernel of known size, to scale HBM byte counters)")
     return ap.parse_args()
 
 
@@ -71,6 +77,16 @@ def main():
     import torch
     import permuted_block_sparse_amd as pbs
     from synthetic import get_config, make_stripe_inputs
+
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] copied {n} bytes device to device")
+        return
 
     cfg = get_config(args.config)
     spec = cfg.spec
@@ -95,6 +111,12 @@ def main():
         pl = pbs.plan(tq, tk, S, t_)
         pbs.prefill(pl, tq, tk, tv, out=out)
         return pl
+
+    if args.profile_once:
+        step()
+        torch.cuda.synchronize()
+        log("[bench] one plan + prefill done")
+        return
 
     for i in range(args.warmup):
         step()

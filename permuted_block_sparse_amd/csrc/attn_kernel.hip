@@ -11,17 +11,20 @@
 // keys; sparse tiles = L_t). Wave w holds rows 32 (w / 4) .. + 31 of query
 // block w % 4; both halves of a block sit on the same SIMD. K and V tiles
 // are gathered into LDS once per workgroup and read by all 8 waves. The two
-// halves of a block exchange their partial tile sums through LDS, so both
-// take the same stop decision from the same bits.
+// halves of a block hand each other their partial tile sums through an LDS
+// mailbox (a pairwise handshake, no workgroup barrier), so both take the
+// same stop decision from the same bits.
 //
 // Pipeline: the local blocks and then the sparse tiles form one sequence of
-// steps. While step s is computed from LDS buffer s % 2, the gather of step
-// s + 1 streams into the other buffer with direct global->LDS loads (no
-// registers), and the tile indices of step s + 2 are fetched.
+// steps. LDS holds two K/V tile buffers. At the start of step s every lane
+// issues the global loads of its share of step s + 1's rows (16 bytes x 4,
+// into registers) and the tile indices of step s + 2; it computes step s
+// from buffer s % 2; at the end it stores the staged rows into the other
+// buffer. One barrier per step.
 //
 // Per wave and 64-key tile:
 //   S^T = K Q^T   : 2 v_mfma_f32_32x32x16_bf16 blocks over d = 128, Q^T
-//                   operands from the wave's LDS copy of its 32 rows;
+//                   operands held in registers for the whole run;
 //   mean of S     : the mean-pooled logit of the 64 x 64 tile (both halves);
 //   online softmax: one query row per lane pair (lane, lane ^ 32), fp32,
 //                   exp2 domain; the running max is raised only when a row's
@@ -32,14 +35,13 @@
 //
 // LDS layouts are "read-native": each tile is stored in exactly the order in
 // which the MFMA operand reads consume it, so every LDS read instruction of
-// a wave touches one contiguous 1 KB (K and Q, ds_read_b128) or 512 B (V,
+// a wave touches one contiguous 1 KB (K, ds_read_b128) or 512 B (V,
 // ds_read_tr16_b64) block -- free of bank conflicts, and every read address
 // is a per-lane base plus an immediate. The gather side picks, per lane,
-// the global 16-byte chunk that belongs at its LDS slot.
+// the global 16-byte chunk that belongs at its LDS slot; the staging stores
+// are contiguous 1 KB blocks too.
 //   K tile: block (kb, s) of 1 KB at (8 kb + s) KB; lane l's 16 bytes hold
 //           K[row 32 kb + l % 32][elements 16 s + 8 (l / 32) .. + 7].
-//   Q rows: per wave, block s of 1 KB; lane l's 16 bytes hold
-//           Q[row l % 32 of the wave's 32][elements 16 s + 8 (l / 32) ..].
 //   V tile: block id = ((2 kb + half) 4 + db) 2 + hi of 512 B at 512 id;
 //           lane l's 8 bytes hold the 4 elements the transposed read of
 //           lane l takes: V[row 32 kb + 16 half + 4 (l / 32) + (l % 16) / 4
@@ -53,8 +55,6 @@ namespace sa {
 constexpr int kTileBytes = kBlock * kHeadDim * 2;  // 16 KB: one K or V tile
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kQBytes = 32 * kHeadDim * 2;          // 8 KB: a wave's Q rows
-constexpr int kLdsBytes = 4 * kTileBytes + kWaves * kQBytes;  // 128 KB
 constexpr float kRescaleSlack = 8.0f;               // log2 units
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
@@ -147,49 +147,58 @@ __device__ __forceinline__ int gather_row_v(int wave, int lane) {
          8 * (lane >> 5);
 }
 
-// Issue the gather of one K tile and one V tile into LDS (asynchronous,
-// completion tracked by the vector memory counter): wave w writes K blocks
-// 2 w, 2 w + 1 and V write blocks 2 w, 2 w + 1 (1 KB per instruction).
-__device__ __forceinline__ void issue_gather(char* kdst, char* vdst,
-                                             const uint16_t* kbase,
-                                             const uint16_t* vbase, int key_k,
-                                             int key_v, int nkeys, int wave,
-                                             int lane) {
+// The 64 bytes one lane moves per step: K blocks 2 w, 2 w + 1 and V write
+// blocks 2 w, 2 w + 1 of its wave w (16 bytes each, see the layouts).
+struct Staged {
+  uint4 k0, k1, v0, v1;
+};
+
+__device__ __forceinline__ Staged load_rows(const uint16_t* kbase,
+                                            const uint16_t* vbase, int key_k,
+                                            int key_v, int nkeys, int wave,
+                                            int lane) {
   key_k = min(max(key_k, 0), nkeys - 1);  // memory-safe for any indices
   key_v = min(max(key_v, 0), nkeys - 1);
   const uint16_t* krow = kbase + (size_t)key_k * kHeadDim + 8 * (lane >> 5);
   const uint16_t* vrow = vbase + (size_t)key_v * kHeadDim +
                          8 * (2 * ((lane >> 3) & 1) + (lane & 1));
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int blk = 2 * wave + j;  // K block (kb, s) = (blk / 8, blk % 8)
-    __builtin_amdgcn_global_load_lds(krow + 16 * (blk & 7),
-                                     (lds_void*)(kdst + blk * 1024), 16, 0, 0);
-    // V write block blk holds tr16 blocks 2 blk, 2 blk + 1, column block
-    // db = blk % 4
-    __builtin_amdgcn_global_load_lds(vrow + 32 * (blk & 3),
-                                     (lds_void*)(vdst + blk * 1024), 16, 0, 0);
-  }
+  const int blk = 2 * wave;  // K block (kb, s) = (blk / 8, blk % 8)
+  Staged r;
+  r.k0 = *reinterpret_cast<const uint4*>(krow + 16 * (blk & 7));
+  r.k1 = *reinterpret_cast<const uint4*>(krow + 16 * ((blk + 1) & 7));
+  // V write block blk holds tr16 blocks 2 blk, 2 blk + 1, column block
+  // db = blk % 4
+  r.v0 = *reinterpret_cast<const uint4*>(vrow + 32 * (blk & 3));
+  r.v1 = *reinterpret_cast<const uint4*>(vrow + 32 * ((blk + 1) & 3));
+  return r;
+}
+
+__device__ __forceinline__ void store_rows(char* kdst, char* vdst,
+                                           const Staged& r, int wave,
+                                           int lane) {
+  const int off = (2 * wave) * 1024 + 16 * lane;
+  *reinterpret_cast<uint4*>(kdst + off) = r.k0;
+  *reinterpret_cast<uint4*>(kdst + off + 1024) = r.k1;
+  *reinterpret_cast<uint4*>(vdst + off) = r.v0;
+  *reinterpret_cast<uint4*>(vdst + off + 1024) = r.v1;
 }
 
 // S^T[kb]: keys kb*32 + 8(r/4) + 4 lh + r%4, query = the lane's row lane%32.
-__device__ __forceinline__ void qk_tile(const char* Kt, const char* Qw,
+__device__ __forceinline__ void qk_tile(const char* Kt, const bf16x8 (&qr)[8],
                                         f32x16 (&sacc)[2], int lane) {
   sacc[0] = f32x16{};
   sacc[1] = f32x16{};
-  bf16x8 op[2][3];
-  auto load = [&](int s, bf16x8 (&o)[3]) {
+  bf16x8 op[2][2];
+  auto load = [&](int s, bf16x8 (&o)[2]) {
     o[0] = *reinterpret_cast<const bf16x8*>(Kt + s * 1024 + 16 * lane);
     o[1] = *reinterpret_cast<const bf16x8*>(Kt + (8 + s) * 1024 + 16 * lane);
-    o[2] = *reinterpret_cast<const bf16x8*>(Qw + s * 1024 + 16 * lane);
   };
   load(0, op[0]);
 #pragma unroll
   for (int s = 0; s < 8; ++s) {
     if (s + 1 < 8) load(s + 1, op[(s + 1) & 1]);
-    const bf16x8(&o)[3] = op[s & 1];
-    sacc[0] = mfma32(o[0], o[2], sacc[0]);
-    sacc[1] = mfma32(o[1], o[2], sacc[1]);
+    sacc[0] = mfma32(op[s & 1][0], qr[s], sacc[0]);
+    sacc[1] = mfma32(op[s & 1][1], qr[s], sacc[1]);
   }
 }
 
@@ -252,11 +261,17 @@ __device__ __forceinline__ void softmax_pv(const char* Vt, f32x16 (&sacc)[2],
   }
 }
 
+// s_waitcnt lgkmcnt(0) (gfx9 encoding; vmcnt and expcnt left unlimited)
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+constexpr int kSpinLimit = 1 << 22;
+
 __global__ __launch_bounds__(kThreads, 1) void k_attn_fwd(AttnArgs a) {
-  // K/V double buffer (4 x 16 KB) + 8 KB of query rows per wave
-  extern __shared__ __attribute__((aligned(1024))) char smem[];
+  // two K/V tile buffers of 2 x 16 KB
+  __shared__ __attribute__((aligned(1024))) char tiles[2][2 * kTileBytes];
   __shared__ int wave_maxrow[kWaves];
-  __shared__ float part[2][kWaves];  // partial tile sums, by step parity
+  __shared__ int busy[2][kWaves];  // per step parity: wave still attending
+  // per-wave mailbox: (step + 1) << 32 | bits of the wave's partial sum
+  __shared__ unsigned long long mailbox[kWaves];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int lq = lane & 31, lh = lane >> 5;
   const int qsub = wave & 3, half = wave >> 2;
@@ -292,13 +307,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_fwd(AttnArgs a) {
   const uint16_t* kbase = a.k + (size_t)bg * a.N * kHeadDim;
   const uint16_t* vbase = a.v + (size_t)bg * a.N * kHeadDim;
 
-  // the wave's 32 query rows -> its own 8 KB of LDS (B-operand order)
-  char* Qw = smem + 4 * kTileBytes + wave * kQBytes;
+  // the lane's query row as Q^T B operands, for the whole run
+  bf16x8 qr[8];
 #pragma unroll
   for (int s = 0; s < 8; ++s)
-    __builtin_amdgcn_global_load_lds(
-        qh + (size_t)iq * kHeadDim + 16 * s + 8 * lh,
-        (lds_void*)(Qw + s * 1024), 16, 0, 0);
+    qr[s] = *reinterpret_cast<const bf16x8*>(qh + (size_t)iq * kHeadDim +
+                                             16 * s + 8 * lh);
 
   f32x16 oacc[4];
 #pragma unroll
@@ -310,7 +324,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_fwd(AttnArgs a) {
   // ---- the step sequence: ndiag local blocks, then the tiles of L_t.
   const int seg0 = t * a.S;
   const int myrow = wave_max_int(iq);
-  if (lane == 0) wave_maxrow[wave] = valid ? myrow : -1;
+  if (lane == 0) {
+    wave_maxrow[wave] = valid ? myrow : -1;
+    mailbox[wave] = 0ull;
+  }
   __syncthreads();
   int wgmax = -1;
 #pragma unroll
@@ -321,40 +338,42 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_fwd(AttnArgs a) {
   const int32_t* Lt =
       a.L + (size_t)bg * a.list_len + (size_t)a.S * t * (t - 1) / 2;
 
-  // key rows this lane gathers for step s (raw keys are clamped only where
-  // they are used, so that step s + 2's key loads are never waited for
-  // inside step s)
+  // Tile indices: every step loads the two indices this lane needs two
+  // steps later (local steps load a harmless in-bounds value and compute
+  // their indices instead).
   const int rk = gather_row_k(wave, lane), rv = gather_row_v(wave, lane);
-  auto step_key = [&](int s, int row) {
-    return s < ndiag ? seg0 + s * kBlock + row
-                     : Lt[(size_t)(s - ndiag) * kBlock + row];
+  auto key_src = [&](int s, int row) -> const int32_t* {
+    return (s >= ndiag && s < nsteps) ? Lt + (size_t)(s - ndiag) * kBlock + row
+                                      : pq + (row & 63);
+  };
+  auto key_of = [&](int s, int row, int raw) {
+    return s < ndiag ? seg0 + s * kBlock + row : raw;
+  };
+  auto stage = [&](int s, int raw_k, int raw_v) {
+    return load_rows(kbase, vbase, key_of(s, rk, raw_k), key_of(s, rv, raw_v),
+                     a.N, wave, lane);
   };
 
-  int nk_k = 0, nk_v = 0;  // keys of the next step to issue
-  issue_gather(smem, smem + kTileBytes, kbase, vbase, step_key(0, rk),
-               step_key(0, rv), a.N, wave, lane);
-  if (nsteps > 1) {
-    nk_k = step_key(1, rk);
-    nk_v = step_key(1, rv);
+  // prologue: step 0's rows into buffer 0, indices of step 1
+  {
+    const Staged r0 = stage(0, *key_src(0, rk), *key_src(0, rv));
+    store_rows(tiles[0], tiles[0] + kTileBytes, r0, wave, lane);
   }
-  __builtin_amdgcn_s_waitcnt(0);
+  int raw_k = *key_src(1, rk), raw_v = *key_src(1, rv);
   __syncthreads();
 
   bool active = valid;
   int n_visit = t > 0 ? ntiles : 0;
   for (int s = 0; s < nsteps; ++s) {
-    const int cur = s & 1;
-    const char* Kt = smem + cur * 2 * kTileBytes;
+    const char* Kt = tiles[s & 1];
     const char* Vt = Kt + kTileBytes;
-    if (s + 1 < nsteps) {
-      char* nk = smem + (cur ^ 1) * 2 * kTileBytes;
-      issue_gather(nk, nk + kTileBytes, kbase, vbase, nk_k, nk_v, a.N, wave,
-                   lane);
-      if (s + 2 < nsteps) {
-        nk_k = step_key(s + 2, rk);
-        nk_v = step_key(s + 2, rv);
-      }
-    }
+    // stage step s + 1's rows and fetch step s + 2's indices
+    const bool more = s + 1 < nsteps;
+    Staged nxt;
+    if (more) nxt = stage(s + 1, raw_k, raw_v);
+    raw_k = *key_src(s + 2, rk);
+    raw_v = *key_src(s + 2, rv);
+
     // local block (s < ndiag): exact causal attention, mass estimate from
     // the mean logit of the whole 64 x 64 block weighted by its visible
     // pairs; sparse tile: estimate, stop test, then attention.
@@ -367,21 +386,33 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_fwd(AttnArgs a) {
                                   : 0;
       nvis = wave_sum_int(nv_lane);
     }
+    // the halves of a block always agree on `compute`
     const bool compute = local ? (valid && nvis > 0) : active;
     if (compute) {
-      qk_tile(Kt, Qw, sacc, lane);
+      qk_tile(Kt, qr, sacc, lane);
       const float ps = wave_sum(lane_sum(sacc));
-      if (lane == 0) part[cur][wave] = ps;
-    }
-    // both halves of each block see both partial sums (the halves of a
-    // block always agree on `compute`)
-    __syncthreads();
-    if (compute) {
-      const float ssum = part[cur][qsub] + part[cur][qsub + 4];
-      const double ex = exp((double)ssum * (a.kappa / (kBlock * kBlock)));
+      const unsigned long long tag = (unsigned long long)(s + 1) << 32;
+      typedef __attribute__((address_space(3))) volatile unsigned long long
+          lds_u64;
+      lds_u64* box = (lds_u64*)mailbox;
+      if (lane == 0) box[wave] = tag | __float_as_uint(ps);
+      // wait for the other half's partial sum of this step (bounded)
+      unsigned long long other;
+      int spins = 0;
+      while (true) {
+        other = box[wave ^ 4];
+        if ((other >> 32) == (unsigned long long)(s + 1) ||
+            ++spins >= kSpinLimit)
+          break;
+        __builtin_amdgcn_s_sleep(1);
+      }
+      const float po = __uint_as_float((uint32_t)other);
+      const float ssum = half == 0 ? ps + po : po + ps;  // same order for both
+      const float ex = __builtin_amdgcn_exp2f(
+          ssum * (float)(a.kappa * 1.4426950408889634 / (kBlock * kBlock)));
       bool take = true;
       if (local) {
-        acc += ((double)nvis / kBlock) * ex;
+        acc += ((double)nvis / kBlock) * (double)ex;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -390,7 +421,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_fwd(AttnArgs a) {
             if (jk > iq) sacc[kb][r] = -INFINITY;
           }
       } else {
-        const double est = kBlock * ex;
+        const double est = kBlock * (double)ex;
         if (est / (acc + est) < a.tau) {
           active = false;
           n_visit = s - ndiag;
@@ -401,9 +432,20 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_fwd(AttnArgs a) {
       }
       if (take) softmax_pv(Vt, sacc, oacc, m, l, a.c2, lane);
     }
-    __builtin_amdgcn_s_waitcnt(0);  // this step's gather and index loads
-    if (!__syncthreads_or(active)) break;
+    // staged rows -> the other buffer (read last in step s - 1, before the
+    // previous barrier), then one barrier, which also combines the waves'
+    // `active` flags
+    if (more) store_rows(tiles[(s + 1) & 1], tiles[(s + 1) & 1] + kTileBytes,
+                         nxt, wave, lane);
+    if (lane == 0) busy[s & 1][wave] = active ? 1 : 0;
+    wait_lgkm0();
+    __builtin_amdgcn_s_barrier();
+    int any = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) any |= busy[s & 1][w];
+    if (!any) break;
   }
+  __builtin_amdgcn_s_waitcnt(0);  // index loads of steps never taken
 
   // ---- epilogue: normalise, round to bf16, scatter to the original rows.
   if (!valid) return;
@@ -427,15 +469,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_fwd(AttnArgs a) {
 
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
   const int total = a.n_groups * a.wg_per_group;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(k_attn_fwd),
-        hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
-  hipLaunchKernelGGL(k_attn_fwd, dim3(total), dim3(kThreads), kLdsBytes, s, a);
+  hipLaunchKernelGGL(k_attn_fwd, dim3(total), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 

@@ -16,11 +16,14 @@
 // same stop decision from the same bits.
 //
 // Pipeline: the local blocks and then the sparse tiles form one sequence of
-// steps. LDS holds two K/V tile buffers. At the start of step s every lane
-// issues the global loads of its share of step s + 1's rows (16 bytes x 4,
-// into registers) and the tile indices of step s + 2; it computes step s
-// from buffer s % 2; at the end it stores the staged rows into the other
-// buffer. One barrier per step.
+// steps. LDS holds two K/V tile buffers. Step s computes S of tile s from
+// buffer s % 2 and posts its partial tile sum; while the other half of the
+// block finishes its own, every lane stores its share of tile s + 1's rows
+// (loaded into registers during step s - 1) into the other buffer and
+// issues the global loads of tile s + 2's rows and step s + 3's indices;
+// then the stop decision and the softmax / PV of tile s. One barrier per
+// step. The rows have a whole step to arrive, and the LDS stores overlap
+// the half-pair handshake instead of the MFMA phases.
 //
 // Per wave and 64-key tile:
 //   S^T = K Q^T   : 2 v_mfma_f32_32x32x16_bf16 blocks over d = 128, Q^T
@@ -354,12 +357,15 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_fwd(AttnArgs a) {
                      a.N, wave, lane);
   };
 
-  // prologue: step 0's rows into buffer 0, indices of step 1
+  // prologue: step 0's rows into buffer 0, step 1's rows into registers,
+  // indices of step 2
   {
     const Staged r0 = stage(0, *key_src(0, rk), *key_src(0, rv));
     store_rows(tiles[0], tiles[0] + kTileBytes, r0, wave, lane);
   }
-  int raw_k = *key_src(1, rk), raw_v = *key_src(1, rv);
+  Staged nxt = {};
+  if (nsteps > 1) nxt = stage(1, *key_src(1, rk), *key_src(1, rv));
+  int raw_k = *key_src(2, rk), raw_v = *key_src(2, rv);
   __syncthreads();
 
   bool active = valid;
@@ -367,12 +373,6 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_fwd(AttnArgs a) {
   for (int s = 0; s < nsteps; ++s) {
     const char* Kt = tiles[s & 1];
     const char* Vt = Kt + kTileBytes;
-    // stage step s + 1's rows and fetch step s + 2's indices
-    const bool more = s + 1 < nsteps;
-    Staged nxt;
-    if (more) nxt = stage(s + 1, raw_k, raw_v);
-    raw_k = *key_src(s + 2, rk);
-    raw_v = *key_src(s + 2, rv);
 
     // local block (s < ndiag): exact causal attention, mass estimate from
     // the mean logit of the whole 64 x 64 block weighted by its visible
@@ -388,14 +388,27 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_fwd(AttnArgs a) {
     }
     // the halves of a block always agree on `compute`
     const bool compute = local ? (valid && nvis > 0) : active;
+    typedef __attribute__((address_space(3))) volatile unsigned long long
+        lds_u64;
+    lds_u64* box = (lds_u64*)mailbox;
+    float ps = 0.f;
     if (compute) {
       qk_tile(Kt, qr, sacc, lane);
-      const float ps = wave_sum(lane_sum(sacc));
-      const unsigned long long tag = (unsigned long long)(s + 1) << 32;
-      typedef __attribute__((address_space(3))) volatile unsigned long long
-          lds_u64;
-      lds_u64* box = (lds_u64*)mailbox;
-      if (lane == 0) box[wave] = tag | __float_as_uint(ps);
+      ps = wave_sum(lane_sum(sacc));
+      if (lane == 0)
+        box[wave] = ((unsigned long long)(s + 1) << 32) | __float_as_uint(ps);
+    }
+    // while the other half finishes its partial sum: step s + 1's rows
+    // (loaded during step s - 1) -> the other buffer, which held step
+    // s - 1's tile (read by every wave before the last barrier); then the
+    // loads of step s + 2's rows and of step s + 3's indices
+    if (s + 1 < nsteps)
+      store_rows(tiles[(s + 1) & 1], tiles[(s + 1) & 1] + kTileBytes, nxt,
+                 wave, lane);
+    if (s + 2 < nsteps) nxt = stage(s + 2, raw_k, raw_v);
+    raw_k = *key_src(s + 3, rk);
+    raw_v = *key_src(s + 3, rv);
+    if (compute) {
       // wait for the other half's partial sum of this step (bounded)
       unsigned long long other;
       int spins = 0;
@@ -421,8 +434,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_fwd(AttnArgs a) {
             if (jk > iq) sacc[kb][r] = -INFINITY;
           }
       } else {
+        // share est / (acc + est) < tau, without the division
         const double est = kBlock * (double)ex;
-        if (est / (acc + est) < a.tau) {
+        if (est < a.tau * (acc + est)) {
           active = false;
           n_visit = s - ndiag;
           take = false;
@@ -432,11 +446,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_fwd(AttnArgs a) {
       }
       if (take) softmax_pv(Vt, sacc, oacc, m, l, a.c2, lane);
     }
-    // staged rows -> the other buffer (read last in step s - 1, before the
-    // previous barrier), then one barrier, which also combines the waves'
-    // `active` flags
-    if (more) store_rows(tiles[(s + 1) & 1], tiles[(s + 1) & 1] + kTileBytes,
-                         nxt, wave, lane);
+    // one barrier, which also combines the waves' `active` flags
     if (lane == 0) busy[s & 1][wave] = active ? 1 : 0;
     wait_lgkm0();
     __builtin_amdgcn_s_barrier();

@@ -27,6 +27,8 @@ CASES = [
      0),
     ("ragged_n640_s128", _spec(1, 2, 1, 640, 22), 128, (0.05, 0.3), 0),
     ("s64_one_block_per_segment", _spec(1, 2, 2, 768, 23), 64, (0.1, 0.4), 0),
+    # 4 of the 8 waves of each workgroup hold no query rows and run ahead
+    ("s64_g2_idle_waves", _spec(1, 2, 1, 768, 23), 64, (0.1, 0.4), 0),
     ("g8_h8_kv1_n512", _spec(1, 8, 1, 512, 24), 128, (0.03,), 0),
     ("single_segment_n256", _spec(1, 2, 1, 256, 25), 256, (0.5,), 0),
     ("single_block_n64", _spec(1, 1, 1, 64, 26, n_vert=2, n_horiz=1,

@@ -36,19 +36,23 @@
 //   O^T += V^T P^T: V^T A operands via ds_read_tr16_b64 transposed reads,
 //                   P^T B operands straight from the S registers.
 //
-// LDS layouts are "read-native": each tile is stored in exactly the order in
-// which the MFMA operand reads consume it, so every LDS read instruction of
-// a wave touches one contiguous 1 KB (K, ds_read_b128) or 512 B (V,
-// ds_read_tr16_b64) block -- free of bank conflicts, and every read address
-// is a per-lane base plus an immediate. The gather side picks, per lane,
-// the global 16-byte chunk that belongs at its LDS slot; the staging stores
-// are contiguous 1 KB blocks too.
+// LDS layouts follow the MFMA operand reads: each read instruction of a wave
+// touches one 1 KB (K, ds_read_b128) or 512 B (V, ds_read_tr16_b64) block,
+// with the lanes' 16-byte slots permuted by an XOR swizzle. The gather is by
+// whole rows: lane L of wave w moves key row 8 w + L / 8 (its K and its V
+// row), 16-byte chunks L % 8 and 8 + L % 8, so each global load instruction
+// covers 8 full 128-byte lines. The swizzle makes both the stores of these
+// chunks and the operand reads free of bank conflicts (64 banks of 4 bytes,
+// 16 lanes of 16 bytes per cycle; also with 32 banks, 8 lanes per cycle).
 //   K tile: block (kb, s) of 1 KB at (8 kb + s) KB; lane l's 16 bytes hold
-//           K[row 32 kb + l % 32][elements 16 s + 8 (l / 32) .. + 7].
+//           K[row 32 kb + l % 32][elements 16 s + 8 (l / 32) .. + 7], at
+//           slot l ^ (2 (s % 4) + l / 32) ^ 8 (l % 2).
 //   V tile: block id = ((2 kb + half) 4 + db) 2 + hi of 512 B at 512 id;
 //           lane l's 8 bytes hold the 4 elements the transposed read of
 //           lane l takes: V[row 32 kb + 16 half + 4 (l / 32) + (l % 16) / 4
-//           + 8 hi][col 32 db + 16 ((l / 16) % 2) + 4 (l % 4) .. + 3].
+//           + 8 hi][col 32 db + 16 ((l / 16) % 2) + 4 (l % 4) .. + 3], in
+//           half l % 2 of 16-byte slot
+//           (l / 2) ^ 2 ((l / 16) % 2) ^ 4 (db % 2).
 
 #include "sa_device.h"
 #include "sa_launch.h"
@@ -140,61 +144,92 @@ __device__ __forceinline__ s16x4 lds_read_tr16(const char* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
 }
 
-// Rows of the K and V tiles whose chunks lane `lane` of wave `wave` moves
-// (one row each per step; see the layouts above).
-__device__ __forceinline__ int gather_row_k(int wave, int lane) {
-  return 32 * (wave >> 2) + (lane & 31);
-}
-__device__ __forceinline__ int gather_row_v(int wave, int lane) {
-  return 16 * (wave >> 1) + 4 * ((lane >> 4) & 1) + ((lane & 7) >> 1) +
-         8 * (lane >> 5);
+// The tile row whose K and V chunks lane `lane` of wave `wave` moves.
+__device__ __forceinline__ int gather_row(int wave, int lane) {
+  return 8 * wave + (lane >> 3);
 }
 
-// The 64 bytes one lane moves per step: K blocks 2 w, 2 w + 1 and V write
-// blocks 2 w, 2 w + 1 of its wave w (16 bytes each, see the layouts).
+// LDS byte offsets of the two K and two V chunks one lane stores (the second
+// of each pair is the first plus 4 KB for K, plus 2 KB for V).
+struct StoreAddr {
+  int k, v;
+};
+__device__ __forceinline__ StoreAddr store_addr(int row, int lane) {
+  const int c = lane & 7;  // 16-byte chunk of the row's first half
+  StoreAddr a;
+  {
+    const int kb = row >> 5, s = c >> 1, b = c & 1;
+    const int l = (row & 31) + 32 * b;
+    const int sig = l ^ (2 * (s & 3) + b) ^ (8 * (l & 1));
+    a.k = (8 * kb + s) * 1024 + 16 * sig;
+  }
+  {
+    const int r8 = row & 7, db = c >> 2;
+    const int slot = (c & 1) + 2 * (r8 & 3) + 8 * ((c & 3) >> 1) + 16 * (r8 >> 2);
+    const int sig = slot ^ (2 * ((c & 3) >> 1)) ^ (4 * (db & 1));
+    const int id =
+        ((2 * (row >> 5) + ((row >> 4) & 1)) * 4 + db) * 2 + ((row >> 3) & 1);
+    a.v = 512 * id + 16 * sig;
+  }
+  return a;
+}
+
+// The 64 bytes one lane moves per step: chunks c and 8 + c (c = lane % 8) of
+// its K row and of its V row.
 struct Staged {
   uint4 k0, k1, v0, v1;
 };
 
 __device__ __forceinline__ Staged load_rows(const uint16_t* kbase,
-                                            const uint16_t* vbase, int key_k,
-                                            int key_v, int nkeys, int wave,
-                                            int lane) {
-  key_k = min(max(key_k, 0), nkeys - 1);  // memory-safe for any indices
-  key_v = min(max(key_v, 0), nkeys - 1);
-  const uint16_t* krow = kbase + (size_t)key_k * kHeadDim + 8 * (lane >> 5);
-  const uint16_t* vrow = vbase + (size_t)key_v * kHeadDim +
-                         8 * (2 * ((lane >> 3) & 1) + (lane & 1));
-  const int blk = 2 * wave;  // K block (kb, s) = (blk / 8, blk % 8)
+                                            const uint16_t* vbase, int key,
+                                            int nkeys, int lane) {
+  key = min(max(key, 0), nkeys - 1);  // memory-safe for any indices
+  const size_t off = (size_t)key * kHeadDim + 8 * (lane & 7);
   Staged r;
-  r.k0 = *reinterpret_cast<const uint4*>(krow + 16 * (blk & 7));
-  r.k1 = *reinterpret_cast<const uint4*>(krow + 16 * ((blk + 1) & 7));
-  // V write block blk holds tr16 blocks 2 blk, 2 blk + 1, column block
-  // db = blk % 4
-  r.v0 = *reinterpret_cast<const uint4*>(vrow + 32 * (blk & 3));
-  r.v1 = *reinterpret_cast<const uint4*>(vrow + 32 * ((blk + 1) & 3));
+  r.k0 = *reinterpret_cast<const uint4*>(kbase + off);
+  r.k1 = *reinterpret_cast<const uint4*>(kbase + off + 64);
+  r.v0 = *reinterpret_cast<const uint4*>(vbase + off);
+  r.v1 = *reinterpret_cast<const uint4*>(vbase + off + 64);
   return r;
 }
 
 __device__ __forceinline__ void store_rows(char* kdst, char* vdst,
-                                           const Staged& r, int wave,
-                                           int lane) {
-  const int off = (2 * wave) * 1024 + 16 * lane;
-  *reinterpret_cast<uint4*>(kdst + off) = r.k0;
-  *reinterpret_cast<uint4*>(kdst + off + 1024) = r.k1;
-  *reinterpret_cast<uint4*>(vdst + off) = r.v0;
-  *reinterpret_cast<uint4*>(vdst + off + 1024) = r.v1;
+                                           const Staged& r, StoreAddr a) {
+  *reinterpret_cast<uint4*>(kdst + a.k) = r.k0;
+  *reinterpret_cast<uint4*>(kdst + a.k + 4096) = r.k1;
+  *reinterpret_cast<uint4*>(vdst + a.v) = r.v0;
+  *reinterpret_cast<uint4*>(vdst + a.v + 2048) = r.v1;
+}
+
+// Per-lane read offsets of the swizzled layouts: K block (kb, s) is read at
+// 1024 (8 kb + s) + kofs[s % 4]; V block id (column block db) at
+// 512 id + vofs[db % 2].
+struct ReadAddr {
+  int kofs[4];
+  int vofs[2];
+};
+__device__ __forceinline__ ReadAddr read_addr(int lane) {
+  ReadAddr a;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    a.kofs[j] = 16 * (lane ^ (2 * j + (lane >> 5)) ^ (8 * (lane & 1)));
+#pragma unroll
+  for (int x = 0; x < 2; ++x)
+    a.vofs[x] =
+        16 * ((lane >> 1) ^ (2 * ((lane >> 4) & 1)) ^ (4 * x)) + 8 * (lane & 1);
+  return a;
 }
 
 // S^T[kb]: keys kb*32 + 8(r/4) + 4 lh + r%4, query = the lane's row lane%32.
 __device__ __forceinline__ void qk_tile(const char* Kt, const bf16x8 (&qr)[8],
-                                        f32x16 (&sacc)[2], int lane) {
+                                        f32x16 (&sacc)[2], const ReadAddr& ra) {
   sacc[0] = f32x16{};
   sacc[1] = f32x16{};
   bf16x8 op[2][2];
   auto load = [&](int s, bf16x8 (&o)[2]) {
-    o[0] = *reinterpret_cast<const bf16x8*>(Kt + s * 1024 + 16 * lane);
-    o[1] = *reinterpret_cast<const bf16x8*>(Kt + (8 + s) * 1024 + 16 * lane);
+    const char* p = Kt + s * 1024 + ra.kofs[s & 3];
+    o[0] = *reinterpret_cast<const bf16x8*>(p);
+    o[1] = *reinterpret_cast<const bf16x8*>(p + 8 * 1024);
   };
   load(0, op[0]);
 #pragma unroll
@@ -218,7 +253,8 @@ __device__ __forceinline__ float lane_sum(const f32x16 (&sacc)[2]) {
 // m is kept in the exp2 domain (m = reference logit * c2).
 __device__ __forceinline__ void softmax_pv(const char* Vt, f32x16 (&sacc)[2],
                                            f32x16 (&oacc)[4], float& m,
-                                           float& l, float c2, int lane) {
+                                           float& l, float c2,
+                                           const ReadAddr& ra) {
   float v = -INFINITY;
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
@@ -256,8 +292,9 @@ __device__ __forceinline__ void softmax_pv(const char* Vt, f32x16 (&sacc)[2],
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
       const int id = ((2 * kb + half) * 4 + db) * 2;
-      const s16x4 lo = lds_read_tr16(Vt + id * 512 + 8 * lane);
-      const s16x4 hi = lds_read_tr16(Vt + (id + 1) * 512 + 8 * lane);
+      const char* p = Vt + id * 512 + ra.vofs[db & 1];
+      const s16x4 lo = lds_read_tr16(p);
+      const s16x4 hi = lds_read_tr16(p + 512);
       const s16x8 cat = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
       oacc[db] = mfma32(__builtin_bit_cast(bf16x8, cat), pb, oacc[db]);
     }
@@ -341,10 +378,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_fwd(AttnArgs a) {
   const int32_t* Lt =
       a.L + (size_t)bg * a.list_len + (size_t)a.S * t * (t - 1) / 2;
 
-  // Tile indices: every step loads the two indices this lane needs two
-  // steps later (local steps load a harmless in-bounds value and compute
-  // their indices instead).
-  const int rk = gather_row_k(wave, lane), rv = gather_row_v(wave, lane);
+  // Tile indices: every step loads the index of the row this lane gathers
+  // three steps later (local steps load a harmless in-bounds value and
+  // compute their indices instead).
+  const int rg = gather_row(wave, lane);
+  const StoreAddr sta = store_addr(rg, lane);
+  const ReadAddr ra = read_addr(lane);
   auto key_src = [&](int s, int row) -> const int32_t* {
     return (s >= ndiag && s < nsteps) ? Lt + (size_t)(s - ndiag) * kBlock + row
                                       : pq + (row & 63);
@@ -352,20 +391,19 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_fwd(AttnArgs a) {
   auto key_of = [&](int s, int row, int raw) {
     return s < ndiag ? seg0 + s * kBlock + row : raw;
   };
-  auto stage = [&](int s, int raw_k, int raw_v) {
-    return load_rows(kbase, vbase, key_of(s, rk, raw_k), key_of(s, rv, raw_v),
-                     a.N, wave, lane);
+  auto stage = [&](int s, int raw) {
+    return load_rows(kbase, vbase, key_of(s, rg, raw), a.N, lane);
   };
 
   // prologue: step 0's rows into buffer 0, step 1's rows into registers,
   // indices of step 2
   {
-    const Staged r0 = stage(0, *key_src(0, rk), *key_src(0, rv));
-    store_rows(tiles[0], tiles[0] + kTileBytes, r0, wave, lane);
+    const Staged r0 = stage(0, *key_src(0, rg));
+    store_rows(tiles[0], tiles[0] + kTileBytes, r0, sta);
   }
   Staged nxt = {};
-  if (nsteps > 1) nxt = stage(1, *key_src(1, rk), *key_src(1, rv));
-  int raw_k = *key_src(2, rk), raw_v = *key_src(2, rv);
+  if (nsteps > 1) nxt = stage(1, *key_src(1, rg));
+  int raw = *key_src(2, rg);
   __syncthreads();
 
   bool active = valid;
@@ -393,7 +431,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_fwd(AttnArgs a) {
     lds_u64* box = (lds_u64*)mailbox;
     float ps = 0.f;
     if (compute) {
-      qk_tile(Kt, qr, sacc, lane);
+      qk_tile(Kt, qr, sacc, ra);
       ps = wave_sum(lane_sum(sacc));
       if (lane == 0)
         box[wave] = ((unsigned long long)(s + 1) << 32) | __float_as_uint(ps);
@@ -404,10 +442,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_fwd(AttnArgs a) {
     // loads of step s + 2's rows and of step s + 3's indices
     if (s + 1 < nsteps)
       store_rows(tiles[(s + 1) & 1], tiles[(s + 1) & 1] + kTileBytes, nxt,
-                 wave, lane);
-    if (s + 2 < nsteps) nxt = stage(s + 2, raw_k, raw_v);
-    raw_k = *key_src(s + 3, rk);
-    raw_v = *key_src(s + 3, rv);
+                 sta);
+    if (s + 2 < nsteps) nxt = stage(s + 2, raw);
+    raw = *key_src(s + 3, rg);
     if (compute) {
       // wait for the other half's partial sum of this step (bounded)
       unsigned long long other;
@@ -444,7 +481,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_fwd(AttnArgs a) {
           acc += est;
         }
       }
-      if (take) softmax_pv(Vt, sacc, oacc, m, l, a.c2, lane);
+      if (take) softmax_pv(Vt, sacc, oacc, m, l, a.c2, ra);
     }
     // one barrier, which also combines the waves' `active` flags
     if (lane == 0) busy[s & 1][wave] = active ? 1 : 0;

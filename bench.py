@@ -31,7 +31,9 @@ BF16_PEAK_TFLOPS = 2500.0     # MI355X dense bf16 MFMA (no sparsity)
 HBM_PEAK_GBS = 8000.0
 TILE_FLOP = 4 * 64 * 64 * 128  # QK^T + PV of one 64 x 64 tile, d = 128
 METRIC = "ms/layer sparse prefill attn @128K; sparsity & MSE; MFMA util vs bf16 peak"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_traffic_n128k.json")
+# query blocks in the CPU oracle's timed sample
+CPU_SAMPLE_BLOCKS = 240
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_attn_fwd_traffic_n128k.json")
 ATTN_SOURCE = os.path.join(ROOT, "permuted_block_sparse_amd", "csrc",
                            "attn_kernel.hip")
 
@@ -107,9 +109,13 @@ def main():
     stream = torch.cuda.current_stream()
     out = torch.empty_like(tq)
 
-    def step(t_=tau):
+    def step(t_=tau, events=None):
         pl = pbs.plan(tq, tk, S, t_)
+        if events is not None:
+            events[0].record(stream)
         pbs.prefill(pl, tq, tk, tv, out=out)
+        if events is not None:
+            events[1].record(stream)
         return pl
 
     if args.profile_once:
@@ -125,13 +131,21 @@ def main():
     torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
+    # HIP events around each prefill launch inside the timed region, on the
+    # stream the kernels run on: the attention kernel's launch duration
+    pre_ev = [(torch.cuda.Event(enable_timing=True),
+               torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
     e0.record(stream)
-    for _ in range(args.steps):
-        pl = step()
+    for i in range(args.steps):
+        pl = step(events=pre_ev[i])
     e1.record(stream)
     torch.cuda.synchronize()
     ms_step = e0.elapsed_time(e1) / args.steps
-    log(f"[bench] timed {args.steps} steps: {ms_step:.3f} ms/step")
+    attn_launch_ms = [a.elapsed_time(b) for a, b in pre_ev]
+    attn_mean = float(np.mean(attn_launch_ms))
+    log(f"[bench] timed {args.steps} steps: {ms_step:.3f} ms/step, "
+        f"prefill launch {attn_mean:.3f} ms")
 
     # ---- stage split with HIP events on the launch stream
     def timed(fn, reps):
@@ -148,8 +162,7 @@ def main():
 
     plan_ms, _ = timed(lambda: pbs.plan(tq, tk, S, tau), max(3, args.steps))
     pl = pbs.plan(tq, tk, S, tau)
-    attn_med, attn_mean = timed(lambda: pbs.prefill(pl, tq, tk, tv, out=out),
-                                max(3, args.steps))
+    attn_med = float(np.median(attn_launch_ms))
     n_I = pl.n_I()
     pi_q = pl.pi_q()
     log(f"[bench] plan {plan_ms:.3f} ms, prefill {attn_med:.3f} ms")
@@ -318,8 +331,9 @@ def extras(args, cfg, q, k, v, tq, tk, tv, pl, out, S, tau, timed):
 
 def cpu_baseline(cfg, q, k, v, S, tau, nb_total):
     """The oracle, as it stands, on a bounded sample of the workload: the
-    full plan of one KV group plus stop points and attention of 24 query
-    blocks of that group; extrapolated linearly to the whole layer (plan x
+    full plan of one KV group plus stop points and attention of
+    CPU_SAMPLE_BLOCKS seeded random query blocks of that group (about 10 s of
+    CPU work at 128K); extrapolated linearly to the whole layer (plan x
     number of KV groups, attention x number of query blocks)."""
     import oracle as O
     try:
@@ -340,8 +354,10 @@ def cpu_baseline(cfg, q, k, v, S, tau, nb_total):
     nb = spec.seq_len // 64
     rng = np.random.default_rng(1)
     blocks = [(0, int(h), int(I)) for h, I in
-              zip(rng.integers(0, G, 24), rng.integers(0, nb, 24))]
-    log("[bench] cpu baseline: oracle stop points + attention of 24 blocks")
+              zip(rng.integers(0, G, CPU_SAMPLE_BLOCKS),
+                  rng.integers(0, nb, CPU_SAMPLE_BLOCKS))]
+    log(f"[bench] cpu baseline: oracle stop points + attention of "
+        f"{len(blocks)} blocks")
     t0 = time.perf_counter()
     n_I, _ = O.stop_points(qs, ks, ref, tau, blocks=blocks)
     O.attend(qs, ks, vs, ref, n_I, blocks=blocks)
@@ -351,8 +367,8 @@ def cpu_baseline(cfg, q, k, v, S, tau, nb_total):
     return {"value": round(est_s * 1e3, 1), "unit": "ms/layer",
             "cores": int(threads), "kind": "oracle",
             "sample": f"oracle plan of 1 of {groups} KV groups "
-                      f"({t_plan:.2f} s) + stop points and attention of 24 "
-                      f"of {nb_total} query blocks ({t_blk * 1e3:.1f} ms "
+                      f"({t_plan:.2f} s) + stop points and attention of "
+                      f"{len(blocks)} of {nb_total} query blocks ({t_blk * 1e3:.1f} ms "
                       f"each), extrapolated linearly to the layer",
             "extrapolated": True}
 

@@ -255,7 +255,17 @@ def extras(args, cfg, q, k, v, tq, tk, tv, pl, out, S, tau, timed):
     pl.set_tau(0.0)
     dense = torch.empty_like(tq)
     dense_ms, _ = timed(lambda: pbs.prefill(pl, tq, tk, tv, out=dense), 2)
+    _, lse_dense = pbs.prefill(pl, tq, tk, tv, out=dense, return_lse=True)
     log(f"[bench] tau=0 (dense) prefill {dense_ms:.3f} ms")
+
+    def recall_stats(lse_sel):
+        # share of each row's dense causal attention mass on its selected
+        # set: exp(lse over Sel(i) - lse over every causal key)
+        r = torch.exp(lse_sel - lse_dense)
+        per_head = r.mean(dim=(0, 2))
+        return {"recall_mean": float("%.4g" % r.mean().item()),
+                "recall_min": float("%.4g" % r.min().item()),
+                "recall_head_mean_min": float("%.4g" % per_head.min().item())}
     sweep = []
     taus = sorted(set(cfg.taus) | {tau})
     for t_ in taus:
@@ -268,15 +278,35 @@ def extras(args, cfg, q, k, v, tq, tk, tv, pl, out, S, tau, timed):
         diff = (o_t.float() - dense.float())
         mse = float((diff * diff).mean().item())
         per_head = (diff * diff).mean(dim=(0, 2, 3)).cpu().numpy()
+        _, lse_t = pbs.prefill(pl, tq, tk, tv, out=o_t, return_lse=True)
         sweep.append({"tau": t_, "prefill_ms": round(ms, 4),
                       "pair_sparsity": round(float(sp), 5),
                       "mse_vs_dense": mse,
                       "mse_per_head_max": float(per_head.max()),
-                      "speedup_vs_dense": round(dense_ms / ms, 3)})
+                      "speedup_vs_dense": round(dense_ms / ms, 3),
+                      **recall_stats(lse_t)})
         log(f"[bench] tau={t_}: {ms:.3f} ms sparsity={sp:.4f} mse={mse:.3g}")
     pl.set_tau(tau)
     res["tau_sweep"] = sweep
     res["dense_prefill_ms"] = round(dense_ms, 4)
+    res["no_early_stop"] = {"note": "SA_NO_EARLYSTOP visits every tile: "
+                                    "the tau = 0 run above",
+                            "prefill_ms": round(dense_ms, 4)}
+
+    # baseline of the component ablation: the dense local window only
+    pl_loc = pbs.plan(tq, tk, S, tau, flags=pbs.SA_LOCAL_ONLY)
+    o_loc = torch.empty_like(tq)
+    loc_ms, _ = timed(lambda: pbs.prefill(pl_loc, tq, tk, tv, out=o_loc), 3)
+    _, lse_loc = pbs.prefill(pl_loc, tq, tk, tv, out=o_loc, return_lse=True)
+    diff = (o_loc.float() - dense.float())
+    sel = B * Hq * T * S * (S + 1) / 2
+    res["local_window_only"] = {
+        "prefill_ms": round(loc_ms, 4),
+        "pair_sparsity": round(1.0 - sel / (B * Hq * N * (N + 1) / 2), 5),
+        "mse_vs_dense": float((diff * diff).mean().item()),
+        **recall_stats(lse_loc)}
+    log(f"[bench] local window only: {res['local_window_only']}")
+    del pl_loc, o_loc, lse_loc
 
     # sampled validation at full size in the timed launch configuration:
     # KV group 0's plan against the oracle, and sampled blocks' stop points

@@ -60,6 +60,11 @@ extern "C" {
 #define SA_NO_QPERM      1u   /* identity query order (ablation)             */
 #define SA_NO_KVPERM     2u   /* identity key/value order (ablation)         */
 #define SA_NO_EARLYSTOP  4u   /* visit every tile (same result as tau = 0)   */
+/* Dense local window only: every query block attends to its own segment
+ * (causal) and to no tile of L_t; n_I = 0 everywhere. The baseline of the
+ * S2O page's component ablation (Key points: keeping only the dense local
+ * window). Takes precedence over SA_NO_EARLYSTOP. */
+#define SA_LOCAL_ONLY    8u
 
 /*
  * Problem description.

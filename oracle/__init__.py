@@ -19,16 +19,21 @@ Pinned parts (see tests/test_oracle_*.py):
     attention for any tau; a closed form for the stop point with constant
     keys; brute-force restricted attention on tiny inputs; brute-force
     ranking of the two orders; worked examples of both orders; a golden
-    fixture in tests/golden/.
+    fixture in tests/golden/;
+  * the dense-local-window-only baseline (SA_LOCAL_ONLY) -- against dense
+    attention of each segment taken as a sequence of its own;
+  * attention recall -- equal to 1 when nothing is skipped, to the
+    logsumexp difference of the selected and the full causal key sets
+    (library logsumexp), and to the own-segment share for SA_LOCAL_ONLY.
 Parity unpinned: the agreement of the sparsity/MSE figures with the numbers
 printed on the S2O summary page (those need real models and datasets).
 """
-from .s2o import (SA_NO_QPERM, SA_NO_KVPERM, SA_NO_EARLYSTOP, Plan,
-                  decode_bf16, fixed_point, dense_causal, plan, stop_points,
-                  attend, s2o_attention, selected_counts, metrics,
-                  restricted_list, kappa_of)
+from .s2o import (SA_NO_QPERM, SA_NO_KVPERM, SA_NO_EARLYSTOP, SA_LOCAL_ONLY,
+                  Plan, decode_bf16, fixed_point, dense_causal, plan,
+                  stop_points, attend, recall, s2o_attention,
+                  selected_counts, metrics, restricted_list, kappa_of)
 
-__all__ = ["SA_NO_QPERM", "SA_NO_KVPERM", "SA_NO_EARLYSTOP", "Plan",
-           "decode_bf16", "fixed_point", "dense_causal", "plan",
-           "stop_points", "attend", "s2o_attention", "selected_counts",
-           "metrics", "restricted_list", "kappa_of"]
+__all__ = ["SA_NO_QPERM", "SA_NO_KVPERM", "SA_NO_EARLYSTOP", "SA_LOCAL_ONLY",
+           "Plan", "decode_bf16", "fixed_point", "dense_causal", "plan",
+           "stop_points", "attend", "recall", "s2o_attention",
+           "selected_counts", "metrics", "restricted_list", "kappa_of"]

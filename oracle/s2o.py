@@ -29,6 +29,7 @@ import numpy as np
 SA_NO_QPERM = 1        # identity query order
 SA_NO_KVPERM = 2       # identity key/value order
 SA_NO_EARLYSTOP = 4    # never stop (same as tau = 0)
+SA_LOCAL_ONLY = 8      # dense local window only: n_I = 0 for every block
 
 BLOCK = 64
 
@@ -320,6 +321,10 @@ def stop_points(q_bits, k_bits, pl: Plan, tau: float,
 
     Returns (n_I [B, Hq, N/64] int64 with -1 for blocks not computed,
     traces dict (b, h, I) -> array of p_k).
+
+    SA_LOCAL_ONLY: no tile of L_t is visited (n_I = 0, empty traces) -- the
+    "dense local window only" baseline of the S2O page's component ablation
+    (Key points).
     """
     B, Hq, N, d = q_bits.shape
     G = Hq // pl.heads_kv
@@ -333,6 +338,11 @@ def stop_points(q_bits, k_bits, pl: Plan, tau: float,
     if blocks is None:
         blocks = [(b, h, I) for b in range(B) for h in range(Hq)
                   for I in range(nb)]
+    if pl.flags & SA_LOCAL_ONLY:
+        for b, h, I in blocks:
+            n_I[b, h, I] = 0
+            traces[(b, h, I)] = np.zeros(0)
+        return n_I, traces
     by_group: Dict[Tuple[int, int, int], list] = {}
     for b, h, I in blocks:
         by_group.setdefault((b, h // G, (I * BLOCK) // S), []).append((h, I))
@@ -407,6 +417,50 @@ def attend(q_bits, k_bits, v_bits, pl: Plan, n_I: np.ndarray,
             o[b, h, rows] = (p @ v[keys]) / s
             lse[b, h, rows] = (m + np.log(s))[:, 0]
     return o, lse
+
+
+def recall(q_bits, k_bits, pl: Plan, n_I: np.ndarray,
+           blocks: Optional[Sequence[Tuple[int, int, int]]] = None):
+    """Attention recall of each row: the share of its dense causal attention
+    mass (softmax of AB-Sparse Eq. (1) over every key j <= i) that falls on
+    its selected set Sel(i) (own-segment keys j <= i plus the first n_I
+    tiles of L_t). 1 when nothing is skipped; float64, [B, Hq, N], NaN in
+    rows of blocks not listed.
+    """
+    B, Hq, N, d = q_bits.shape
+    G = Hq // pl.heads_kv
+    S = pl.segment
+    kap = kappa_of(d)
+    r = np.full((B, Hq, N), np.nan)
+    nb = N // BLOCK
+    if blocks is None:
+        blocks = [(b, h, I) for b in range(B) for h in range(Hq)
+                  for I in range(nb)]
+    by_head: Dict[Tuple[int, int], list] = {}
+    for b, h, I in blocks:
+        by_head.setdefault((b, h), []).append(I)
+    for (b, h), Is in sorted(by_head.items()):
+        g = h // G
+        q = decode_bf16(q_bits[b, h])
+        k = decode_bf16(k_bits[b, g])
+        for I in Is:
+            rows = pl.pi_q[b, h, I * BLOCK:(I + 1) * BLOCK]
+            t = (I * BLOCK) // S
+            top = int(rows.max()) + 1
+            z = kap * (q[rows] @ k[:top].T)
+            j = np.arange(top)
+            causal = j[None, :] <= rows[:, None]
+            z[~causal] = -np.inf
+            w = np.exp(z - z.max(axis=1, keepdims=True))
+            sel = causal & (j[None, :] >= t * S)      # own segment, j <= i
+            n = int(n_I[b, h, I])
+            if t > 0 and n > 0:
+                far = restricted_list(pl, b, g, t)[:n * BLOCK]
+                mark = np.zeros(top, dtype=bool)
+                mark[far[far < top]] = True
+                sel |= mark[None, :]
+            r[b, h, rows] = (w * sel).sum(axis=1) / w.sum(axis=1)
+    return r
 
 
 def s2o_attention(q_bits, k_bits, v_bits, segment: int, tau: float,

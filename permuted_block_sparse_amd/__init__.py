@@ -21,10 +21,11 @@ import torch
 
 from . import _lib
 from ._lib import (SA_NO_QPERM, SA_NO_KVPERM, SA_NO_EARLYSTOP,
-                   SparseAttnError)
+                   SA_LOCAL_ONLY, SparseAttnError)
 
 __all__ = ["plan", "prefill", "SparsePlan", "SA_NO_QPERM", "SA_NO_KVPERM",
-           "SA_NO_EARLYSTOP", "SparseAttnError", "workspace_bytes"]
+           "SA_NO_EARLYSTOP", "SA_LOCAL_ONLY", "SparseAttnError",
+           "workspace_bytes"]
 
 _EXPORT_DTYPES = {
     _lib.SA_EXPORT_PI_K: np.int32, _lib.SA_EXPORT_PI_Q: np.int32,

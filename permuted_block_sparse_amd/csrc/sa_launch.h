@@ -70,6 +70,7 @@ struct AttnArgs {
   double tau;
   double kappa;
   float c2;  // kappa * log2(e)
+  int local_only;  // 1: no tile of L_t is visited (dense local window only)
 };
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
 

@@ -43,7 +43,8 @@ int validate(const sa_params* p) {
   if ((long long)p->batch * p->heads_q * p->seq_len > (1ll << 31) / 2)
     return SA_ERR_UNSUPPORTED_SHAPE;
   if (!(p->tau >= 0.0) || std::isinf(p->tau)) return SA_ERR_INVALID_ARG;
-  if (p->flags & ~(SA_NO_QPERM | SA_NO_KVPERM | SA_NO_EARLYSTOP))
+  if (p->flags &
+      ~(SA_NO_QPERM | SA_NO_KVPERM | SA_NO_EARLYSTOP | SA_LOCAL_ONLY))
     return SA_ERR_INVALID_ARG;
   return SA_OK;
 }
@@ -242,6 +243,7 @@ int sparse_attn_prefill(const sa_plan* plan, const void* q, const void* k,
   a.wg_per_group = (qblocks + 3) / 4;
   a.n_groups = d.B * d.Hkv * d.T;
   a.tau = (plan->p.flags & SA_NO_EARLYSTOP) ? 0.0 : plan->p.tau;
+  a.local_only = (plan->p.flags & SA_LOCAL_ONLY) ? 1 : 0;
   a.kappa = 1.0 / std::sqrt((double)kHeadDim);
   a.c2 = (float)(a.kappa * 1.4426950408889634074);
   return hip_status(launch_attention(a, stream));

@@ -409,6 +409,67 @@ def check_monotone_tau(O):
     assert np.all(prev == 0)
 
 
+
+# ------------------------------------------------- baselines and diagnostics
+
+def check_local_only(O):
+    """SA_LOCAL_ONLY visits no tile (also with SA_NO_EARLYSTOP); every row's
+    output and lse equal dense causal attention of its own segment taken as
+    a sequence of its own (the dense-local-window-only baseline of the S2O
+    page's component ablation)."""
+    q, k, v = _stripe(Hq=2, Hkv=1, N=512, d=32, seed=9)
+    S = 128
+    for flags in (O.SA_LOCAL_ONLY, O.SA_LOCAL_ONLY | O.SA_NO_EARLYSTOP):
+        pl = O.plan(q, k, S, flags=flags)
+        n_I, _ = O.stop_points(q, k, pl, 0.0)
+        assert np.all(n_I == 0)
+        o, lse = O.attend(q, k, v, pl, n_I)
+        for t in range(512 // S):
+            sl = slice(t * S, (t + 1) * S)
+            od, ld = O.dense_causal(np.ascontiguousarray(q[:, :, sl]),
+                                    np.ascontiguousarray(k[:, :, sl]),
+                                    np.ascontiguousarray(v[:, :, sl]))
+            assert np.abs(o[:, :, sl] - od).max() < 1e-12
+            assert np.abs(lse[:, :, sl] - ld).max() < 1e-12
+
+
+def check_recall(O):
+    """Attention recall: 1 when nothing is skipped (tau = 0); otherwise
+    exp(lse over Sel(i) - lse over every causal key) with the second from
+    torch.logsumexp; within (0, 1] and non-increasing in tau; for
+    SA_LOCAL_ONLY the share of the own-segment keys, from explicit index
+    sets and torch.logsumexp."""
+    q, k, v = _stripe(Hq=2, Hkv=1, N=512, d=32, seed=10)
+    N, S, d = 512, 128, 32
+    tq = torch.from_numpy(O.decode_bf16(q))
+    tk = torch.from_numpy(O.decode_bf16(k)).repeat_interleave(2, 1)
+    z = (tq @ tk.transpose(-1, -2)) / math.sqrt(d)
+    i = torch.arange(N)
+    causal = i[None, :] <= i[:, None]
+    lse_dense = torch.logsumexp(z.masked_fill(~causal, float("-inf")),
+                                -1).numpy()
+    pl = O.plan(q, k, S)
+    n0, _ = O.stop_points(q, k, pl, 0.0)
+    assert np.abs(O.recall(q, k, pl, n0) - 1.0).max() < 1e-12
+    prev = None
+    for tau in (0.1, 0.3, 0.7):
+        n_I, _ = O.stop_points(q, k, pl, tau)
+        assert n_I.sum() < n0.sum()
+        _, lse_sel = O.attend(q, k, v, pl, n_I)
+        r = O.recall(q, k, pl, n_I)
+        assert np.abs(r - np.exp(lse_sel - lse_dense)).max() < 1e-10
+        assert (r > 0).all() and (r <= 1 + 1e-12).all()
+        if prev is not None:
+            assert (r <= prev + 1e-12).all()
+        prev = r
+    pll = O.plan(q, k, S, flags=O.SA_LOCAL_ONLY)
+    nl, _ = O.stop_points(q, k, pll, 0.0)
+    own = causal & ((i[None, :] // S) == (i[:, None] // S))
+    lse_own = torch.logsumexp(z.masked_fill(~own, float("-inf")), -1).numpy()
+    assert np.abs(O.recall(q, k, pll, nl) - np.exp(lse_own - lse_dense)
+                  ).max() < 1e-10
+
+
 ALL_CHECKS = [
     check_fixed_point, check_dense_vs_sdpa, check_dense_closed_forms,
     check_worked_orders, check_stripe_score_bruteforce, check_plan_invariants,
@@ -416,5 +477,5 @@ ALL_CHECKS = [
     check_single_segment_is_dense, check_bruteforce_restricted,
     check_constant_keys_closed_form, check_strict_stop,
     check_two_level_closed_form, check_permuted_block_closed_form,
-    check_monotone_tau,
+    check_monotone_tau, check_local_only, check_recall,
 ]

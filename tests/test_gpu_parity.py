@@ -36,6 +36,10 @@ CASES = [
     ("no_qperm", _spec(1, 4, 1, 1024, 27), 256, (0.05,), O.SA_NO_QPERM),
     ("no_kvperm", _spec(1, 4, 1, 1024, 28), 256, (0.05,), O.SA_NO_KVPERM),
     ("no_earlystop", _spec(1, 2, 1, 1024, 29), 256, (0.2,), O.SA_NO_EARLYSTOP),
+    ("local_only", _spec(1, 4, 2, 1024, 32), 256, (0.0, 0.05),
+     O.SA_LOCAL_ONLY),
+    ("local_only_no_earlystop", _spec(1, 2, 1, 640, 33), 128, (0.0,),
+     O.SA_LOCAL_ONLY | O.SA_NO_EARLYSTOP),
     ("s4096_merge_sort_n8192", _spec(1, 2, 1, 8192, 30, n_vert=64,
                                      window=128), 4096, (0.02,), 0),
 ]
@@ -83,6 +87,28 @@ def test_tau0_is_dense_and_kv_order_invariant():
     assert np.array_equal(g2["L"], pl.L)
     assert np.array_equal(g2["pi_q"], pl.pi_q)
     assert_outputs_close(g2["o"], od, g2["lse"], ld)
+
+
+def test_recall_from_lse():
+    """Attention recall from two GPU runs, exp(lse at tau - lse at tau = 0),
+    against the oracle's brute-force recall (the share of each row's dense
+    causal attention mass on its selected set); also for the dense local
+    window only."""
+    spec = _spec(1, 4, 2, 1024, 34)
+    q, k, v = make_stripe_inputs(spec)
+    S = 256
+    say("[recall] tau = 0 reference run")
+    g0 = run_gpu(q, k, v, S, 0.0)
+    for tau, flags in ((0.05, 0), (0.3, 0), (0.0, O.SA_LOCAL_ONLY)):
+        say(f"[recall] tau={tau} flags={flags}")
+        g = run_gpu(q, k, v, S, tau, flags)
+        pl = O.plan(q, k, S, flags=flags)
+        n_I = g["n_I"].astype(np.int64)  # recall of the GPU's own selection
+        r_ref = O.recall(q, k, pl, n_I)
+        r_gpu = np.exp(g["lse"] - g0["lse"])
+        assert np.abs(r_gpu - r_ref).max() <= 5e-3, np.abs(r_gpu - r_ref).max()
+        if flags == 0 and tau > 0.1:
+            assert r_ref.mean() < 1.0 - 1e-6  # something was skipped
 
 
 def test_deterministic():

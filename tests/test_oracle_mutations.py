@@ -14,6 +14,12 @@ SRC = pathlib.Path(S2O.__file__).read_text()
 
 # (name, exact text in oracle/s2o.py, replacement)
 MUTANTS = [
+    ("local_only_ignored", "    if pl.flags & SA_LOCAL_ONLY:\n", "    if False:\n"),
+    ("recall_strict_causal", "causal = j[None, :] <= rows[:, None]",
+     "causal = j[None, :] < rows[:, None]"),
+    ("recall_no_far", "                sel |= mark[None, :]\n", "\n"),
+    ("recall_segment_off_by_one", "sel = causal & (j[None, :] >= t * S)",
+     "sel = causal & (j[None, :] > t * S)"),
     ("floor_not_rint", "y = np.rint(x * 256.0)", "y = np.floor(x * 256.0)"),
     ("scale_128", "y = np.rint(x * 256.0)", "y = np.rint(x * 128.0)"),
     ("clip_bounds", "np.clip(y, -32768.0, 32767.0)",

@@ -308,6 +308,26 @@ def extras(args, cfg, q, k, v, tq, tk, tv, pl, out, S, tau, timed):
     log(f"[bench] local window only: {res['local_window_only']}")
     del pl_loc, o_loc, lse_loc
 
+    # segment-local key order (the PBS-Attn variant) at the same tau
+    plan_seg_ms, _ = timed(
+        lambda: pbs.plan(tq, tk, S, tau, flags=pbs.SA_SEGMENT_KV), 3)
+    pl_seg = pbs.plan(tq, tk, S, tau, flags=pbs.SA_SEGMENT_KV)
+    o_seg = torch.empty_like(tq)
+    seg_ms, _ = timed(lambda: pbs.prefill(pl_seg, tq, tk, tv, out=o_seg), 3)
+    _, lse_seg = pbs.prefill(pl_seg, tq, tk, tv, out=o_seg, return_lse=True)
+    n_seg = pl_seg.n_I()
+    sel = B * Hq * T * S * (S + 1) / 2 + 4096.0 * n_seg.sum()
+    diff = (o_seg.float() - dense.float())
+    res["segment_kv_order"] = {
+        "tau": tau, "plan_ms": round(plan_seg_ms, 4),
+        "prefill_ms": round(seg_ms, 4),
+        "pair_sparsity": round(float(1.0 - sel / (B * Hq * N * (N + 1) / 2)),
+                               5),
+        "mse_vs_dense": float((diff * diff).mean().item()),
+        **recall_stats(lse_seg)}
+    log(f"[bench] segment-local KV order: {res['segment_kv_order']}")
+    del pl_seg, o_seg, lse_seg
+
     # sampled validation at full size in the timed launch configuration:
     # KV group 0's plan against the oracle, and sampled blocks' stop points
     # and outputs (and the dense reference on sampled rows)

@@ -65,6 +65,14 @@ extern "C" {
  * S2O page's component ablation (Key points: keeping only the dense local
  * window). Takes precedence over SA_NO_EARLYSTOP. */
 #define SA_LOCAL_ONLY    8u
+/* Segment-local key/value order (the PBS-Attn page's permutation inside
+ * causal segments, abstract): pi_K sorts the keys of each segment by their
+ * stripe score (descending, ties by index); its 64-key chunks are the tiles,
+ * and segment t visits the tiles of segments 0 .. t - 1 by tile score (sum
+ * of the scores of its keys) descending, ties by tile index. L_t keeps its
+ * layout. SA_NO_KVPERM takes precedence; sparse_attn_plan_set_kv_order
+ * returns SA_ERR_INVALID_ARG for a plan built with this flag. */
+#define SA_SEGMENT_KV   16u
 
 /*
  * Problem description.
@@ -173,7 +181,8 @@ int sparse_attn_plan_export(const sa_plan* plan, int what, void* host_dst,
 /* Replace the global KV order by `pi_k` (device int32 [B, Hkv, N], each row
  * a permutation of 0..N-1, not checked) and rebuild everything that depends
  * on it (restricted lists, contrast vectors, query scores and order). For
- * tests: with tau = 0 the output must not depend on the KV order. */
+ * tests: with tau = 0 the output must not depend on the KV order.
+ * Returns SA_ERR_INVALID_ARG for a plan built with SA_SEGMENT_KV. */
 int sparse_attn_plan_set_kv_order(sa_plan* plan, const void* pi_k,
                                   hipStream_t stream);
 

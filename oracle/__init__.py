@@ -24,16 +24,20 @@ Pinned parts (see tests/test_oracle_*.py):
     attention of each segment taken as a sequence of its own;
   * attention recall -- equal to 1 when nothing is skipped, to the
     logsumexp difference of the selected and the full causal key sets
-    (library logsumexp), and to the own-segment share for SA_LOCAL_ONLY.
+    (library logsumexp), and to the own-segment share for SA_LOCAL_ONLY;
+  * the segment-local key order (SA_SEGMENT_KV) -- a hand-derived example
+    of the tile order, invariants, and tau = 0 reproducing dense attention.
 Parity unpinned: the agreement of the sparsity/MSE figures with the numbers
 printed on the S2O summary page (those need real models and datasets).
 """
 from .s2o import (SA_NO_QPERM, SA_NO_KVPERM, SA_NO_EARLYSTOP, SA_LOCAL_ONLY,
+                  SA_SEGMENT_KV,
                   Plan, decode_bf16, fixed_point, dense_causal, plan,
                   stop_points, attend, recall, s2o_attention,
                   selected_counts, metrics, restricted_list, kappa_of)
 
 __all__ = ["SA_NO_QPERM", "SA_NO_KVPERM", "SA_NO_EARLYSTOP", "SA_LOCAL_ONLY",
+           "SA_SEGMENT_KV",
            "Plan", "decode_bf16", "fixed_point", "dense_causal", "plan",
            "stop_points", "attend", "recall", "s2o_attention",
            "selected_counts", "metrics", "restricted_list", "kappa_of"]

@@ -30,6 +30,7 @@ SA_NO_QPERM = 1        # identity query order
 SA_NO_KVPERM = 2       # identity key/value order
 SA_NO_EARLYSTOP = 4    # never stop (same as tau = 0)
 SA_LOCAL_ONLY = 8      # dense local window only: n_I = 0 for every block
+SA_SEGMENT_KV = 16     # segment-local key order, tiles visited by tile score
 
 BLOCK = 64
 
@@ -192,6 +193,18 @@ def plan(q_bits, k_bits, segment: int, block: int = BLOCK,
     identity (the other steps are unchanged). ``kv_order`` ([B, Hkv, N])
     replaces pi_K by a given permutation (a test hook: with tau = 0 the
     output must not depend on it).
+
+    SA_SEGMENT_KV replaces steps 3 and 4 by the segment-local key order of
+    the PBS-Attn page (tokens permuted inside causal segments, abstract):
+    pi_K sorts the keys of each segment [u S, u S + S) by v descending, ties
+    by index; its 64-key chunks are the tiles (S is a multiple of 64, so no
+    tile crosses a segment); L_t lists the tiles of segments 0 .. t - 1 by
+    tile score (sum of v over the tile) descending, ties by tile index.
+    READING: the PBS-Attn page gives the permutation inside segments but no
+    visiting order; most-to-least-important visiting (S2O summary, Summary)
+    needs one, and the tile score is the mean-pooled stripe score of the
+    tile up to the factor 64. SA_NO_KVPERM takes precedence; ``kv_order``
+    cannot be combined with it.
     """
     B, Hq, Hkv, N, d = _check_shape(q_bits, k_bits, segment, block)
     G = Hq // Hkv
@@ -218,17 +231,32 @@ def plan(q_bits, k_bits, segment: int, block: int = BLOCK,
             v = kx @ P
             key_score[b, g] = v
             # 3. global order: v descending, then index ascending
+            segment_kv = bool(flags & SA_SEGMENT_KV) and not (
+                flags & SA_NO_KVPERM)
             if kv_order is not None:
+                if segment_kv:
+                    raise ValueError("kv_order with SA_SEGMENT_KV")
                 order = np.asarray(kv_order[b, g], dtype=np.int64)
                 assert np.array_equal(np.sort(order), idx)
             elif flags & SA_NO_KVPERM:
                 order = idx.copy()
+            elif segment_kv:
+                order = np.concatenate([
+                    seg[np.lexsort((seg, -v[seg]))]
+                    for seg in (idx[u * S:(u + 1) * S] for u in range(T))])
             else:
                 order = np.lexsort((idx, -v))
             pi_k[b, g] = order
-            # 4. causal restriction, 5. contrast vectors
+            # 4. causal restriction (or the tile order of the segment-local
+            # variant), 5. contrast vectors
             for t in range(1, T):
-                Lt = order[order < t * S]
+                if segment_kv:
+                    tiles = order[:t * S].reshape(-1, BLOCK)
+                    tscore = v[tiles].sum(axis=1)
+                    tid = np.arange(len(tiles))
+                    Lt = tiles[np.lexsort((tid, -tscore))].reshape(-1)
+                else:
+                    Lt = order[order < t * S]
                 assert len(Lt) == t * S
                 o = list_offset(S, t)
                 L[b, g, o:o + t * S] = Lt

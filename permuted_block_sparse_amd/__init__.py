@@ -21,10 +21,11 @@ import torch
 
 from . import _lib
 from ._lib import (SA_NO_QPERM, SA_NO_KVPERM, SA_NO_EARLYSTOP,
-                   SA_LOCAL_ONLY, SparseAttnError)
+                   SA_LOCAL_ONLY, SA_SEGMENT_KV, SparseAttnError)
 
 __all__ = ["plan", "prefill", "SparsePlan", "SA_NO_QPERM", "SA_NO_KVPERM",
-           "SA_NO_EARLYSTOP", "SA_LOCAL_ONLY", "SparseAttnError",
+           "SA_NO_EARLYSTOP", "SA_LOCAL_ONLY", "SA_SEGMENT_KV",
+           "SparseAttnError",
            "workspace_bytes"]
 
 _EXPORT_DTYPES = {

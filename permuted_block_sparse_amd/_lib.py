@@ -19,6 +19,7 @@ SA_NO_QPERM = 1
 SA_NO_KVPERM = 2
 SA_NO_EARLYSTOP = 4
 SA_LOCAL_ONLY = 8
+SA_SEGMENT_KV = 16
 
 SA_EXPORT_PI_K = 0
 SA_EXPORT_PI_Q = 1

@@ -398,6 +398,63 @@ __global__ __launch_bounds__(256) void k_restrict_write(
 // --------------------------------------------------------------------------
 // Launchers
 // --------------------------------------------------------------------------
+// --------------------------------------------------------------------------
+// Segment-local key order (the PBS-Attn page's permutation inside causal
+// segments): pi_K sorts the keys of each segment by v; its 64-key chunks are
+// the tiles; segment t visits the tiles of segments 0 .. t - 1 by tile score
+// (the sum of v over the tile, exact int64) descending, ties by tile index.
+// --------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_tile_score(
+    const int64_t* __restrict__ v, const int32_t* __restrict__ pi_k,
+    int64_t* __restrict__ tscore, int N, long long ntiles_total) {
+  // one wave per tile, one key per lane
+  const long long tile = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (tile >= ntiles_total) return;
+  const int lane = threadIdx.x & 63;
+  const long long bg = tile / (N / 64);
+  const int key = min(max(pi_k[tile * 64 + lane], 0), N - 1);
+  int64_t s = v[bg * N + key];
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) s += shfl_xor_i64(s, o);
+  if (lane == 0) tscore[tile] = s;
+}
+
+__global__ __launch_bounds__(256) void k_segment_tiles(
+    const int64_t* __restrict__ tscore, const int32_t* __restrict__ pi_k,
+    int32_t* __restrict__ L, int N, int S, int T, long long list_len) {
+  __shared__ uint64_t key[kMaxTiles];
+  __shared__ int32_t idx[kMaxTiles];
+  const int t = 1 + blockIdx.x % (T - 1);
+  const long long bg = blockIdx.x / (T - 1);
+  const int nt = t * (S / 64);  // tiles of segments 0 .. t - 1
+  int np2 = 1;
+  while (np2 < nt) np2 <<= 1;
+  const int64_t* ts = tscore + bg * (N / 64);
+  for (int i = threadIdx.x; i < np2; i += 256) {
+    if (i < nt) {
+      key[i] = desc_key(ts[i]);
+      idx[i] = i;
+    } else {
+      key[i] = ~0ull;
+      idx[i] = 0x7fffffff;
+    }
+  }
+  __syncthreads();
+  for (int kk = 2; kk <= np2; kk <<= 1) {
+    for (int j = kk >> 1; j > 0; j >>= 1) {
+      for (int p = threadIdx.x; p < (np2 >> 1); p += 256) {
+        const int i = (p / j) * 2 * j + (p % j);
+        cmp_swap(key, idx, i, i + j, (i & kk) == 0);
+      }
+      __syncthreads();
+    }
+  }
+  int32_t* Lt = L + bg * list_len + (long long)S * t * (t - 1) / 2;
+  const int32_t* pk = pi_k + bg * N;
+  for (int i = threadIdx.x; i < nt * 64; i += 256)
+    Lt[i] = pk[idx[i >> 6] * 64 + (i & 63)];
+}
+
 hipError_t launch_pool_q(const PlanDims& d, const uint16_t* q, int64_t* part,
                          hipStream_t s) {
   hipLaunchKernelGGL(k_pool_q, dim3(d.B * d.Hq * d.n_pool_chunks), dim3(256), 0,
@@ -499,6 +556,22 @@ hipError_t launch_restrict(const PlanDims& d, const int32_t* pi_k,
   hipLaunchKernelGGL(k_restrict_write, dim3(nbg * d.n_restrict_chunks),
                      dim3(256), 0, s, pi_k, cum, L, d.N, d.S, d.T,
                      d.n_restrict_chunks, (long long)d.list_len);
+  return hipGetLastError();
+}
+
+hipError_t launch_segment_tiles(const PlanDims& d, const int64_t* v,
+                                const int32_t* pi_k, int64_t* tscore,
+                                int32_t* L, hipStream_t s) {
+  if (d.T < 2) return hipSuccess;
+  const long long nbg = (long long)d.B * d.Hkv;
+  const long long ntiles = nbg * (d.N / 64);
+  hipLaunchKernelGGL(k_tile_score, dim3((unsigned)((ntiles + 3) / 4)),
+                     dim3(256), 0, s, v, pi_k, tscore, d.N, ntiles);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_segment_tiles, dim3((unsigned)(nbg * (d.T - 1))),
+                     dim3(256), 0, s, tscore, pi_k, L, d.N, d.S, d.T,
+                     (long long)d.list_len);
   return hipGetLastError();
 }
 

@@ -13,6 +13,7 @@ constexpr int kPoolRows = 1024;      // rows per pooling workgroup
 constexpr int kScoreRows = 256;      // rows per scoring workgroup
 constexpr int kSortChunk = 4096;     // elements sorted in LDS by one workgroup
 constexpr int kRestrictChunk = 4096; // pi_K entries per restriction workgroup
+constexpr int kMaxTiles = 2048;      // N / 64 at the largest supported N
 
 struct PlanDims {
   int B, Hq, Hkv, N, S, T, G;
@@ -49,6 +50,11 @@ hipError_t launch_segmented_argsort(const int64_t* score, int n_seg,
                                     int32_t* idx_b, int32_t* out,
                                     hipStream_t s);
 hipError_t launch_iota(int32_t* out, size_t n, int rowlen, hipStream_t s);
+// Segment-local key order: tile scores of pi_K's 64-key chunks (tscore,
+// int64 [B Hkv N / 64]) and the lists L_t (tiles of segments < t by score).
+hipError_t launch_segment_tiles(const PlanDims& d, const int64_t* v,
+                                const int32_t* pi_k, int64_t* tscore,
+                                int32_t* L, hipStream_t s);
 hipError_t launch_restrict(const PlanDims& d, const int32_t* pi_k,
                            int32_t* cnt, int32_t* cum, int32_t* L,
                            hipStream_t s);

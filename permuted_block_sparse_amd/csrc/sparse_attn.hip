@@ -44,7 +44,8 @@ int validate(const sa_params* p) {
     return SA_ERR_UNSUPPORTED_SHAPE;
   if (!(p->tau >= 0.0) || std::isinf(p->tau)) return SA_ERR_INVALID_ARG;
   if (p->flags &
-      ~(SA_NO_QPERM | SA_NO_KVPERM | SA_NO_EARLYSTOP | SA_LOCAL_ONLY))
+      ~(SA_NO_QPERM | SA_NO_KVPERM | SA_NO_EARLYSTOP | SA_LOCAL_ONLY |
+        SA_SEGMENT_KV))
     return SA_ERR_INVALID_ARG;
   return SA_OK;
 }
@@ -118,13 +119,25 @@ int hip_status(hipError_t e) { return e == hipSuccess ? SA_OK : SA_ERR_HIP; }
 
 // Everything that depends on the global KV order: restricted lists,
 // contrast vectors, query scores and the query order.
+bool segment_kv(const sa_params& p) {
+  return (p.flags & SA_SEGMENT_KV) && !(p.flags & SA_NO_KVPERM);
+}
+
 int build_from_kv_order(sa_plan* pl, hipStream_t s) {
   const PlanDims& d = pl->d;
   hipError_t e;
-  e = launch_restrict(d, pl->at<int32_t>(pl->lay.pi_k),
-                      pl->at<int32_t>(pl->lay.rcnt),
-                      pl->at<int32_t>(pl->lay.rcum), pl->at<int32_t>(pl->lay.L),
-                      s);
+  if (segment_kv(pl->p)) {
+    // tile scores go to the first sort buffer, free until the query sort
+    e = launch_segment_tiles(d, pl->at<int64_t>(pl->lay.vscore),
+                             pl->at<int32_t>(pl->lay.pi_k),
+                             pl->at<int64_t>(pl->lay.key_a),
+                             pl->at<int32_t>(pl->lay.L), s);
+  } else {
+    e = launch_restrict(d, pl->at<int32_t>(pl->lay.pi_k),
+                        pl->at<int32_t>(pl->lay.rcnt),
+                        pl->at<int32_t>(pl->lay.rcum),
+                        pl->at<int32_t>(pl->lay.L), s);
+  }
   if (e != hipSuccess) return SA_ERR_HIP;
   e = launch_contrast(d, static_cast<const uint16_t*>(pl->k),
                       pl->at<int32_t>(pl->lay.L),
@@ -198,6 +211,12 @@ int sparse_attn_plan(const sa_params* p, const void* q, const void* k,
     const size_t nbg = (size_t)d.B * d.Hkv;
     if (p->flags & SA_NO_KVPERM)
       e = launch_iota(pl->at<int32_t>(lay.pi_k), nbg * d.N, d.N, stream);
+    else if (segment_kv(*p))
+      e = launch_segmented_argsort(
+          pl->at<int64_t>(lay.vscore), (int)(nbg * d.T), d.S, d.N,
+          pl->at<uint64_t>(lay.key_a), pl->at<int32_t>(lay.idx_a),
+          pl->at<uint64_t>(lay.key_b), pl->at<int32_t>(lay.idx_b),
+          pl->at<int32_t>(lay.pi_k), stream);
     else
       e = launch_segmented_argsort(
           pl->at<int64_t>(lay.vscore), (int)nbg, d.N, d.N,
@@ -300,6 +319,8 @@ int sparse_attn_plan_export(const sa_plan* plan, int what, void* host_dst,
 int sparse_attn_plan_set_kv_order(sa_plan* plan, const void* pi_k,
                                   hipStream_t stream) {
   if (plan == nullptr || pi_k == nullptr) return SA_ERR_NULL_POINTER;
+  // a segment-local order's tiles must not mix segments: no injection
+  if (segment_kv(plan->p)) return SA_ERR_INVALID_ARG;
   const size_t bytes = (size_t)plan->d.B * plan->d.Hkv * plan->d.N *
                        sizeof(int32_t);
   hipError_t e = hipMemcpyAsync(plan->ws + plan->lay.pi_k, pi_k, bytes,

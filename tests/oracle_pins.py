@@ -205,7 +205,8 @@ def check_tau0_is_dense(O):
     q, k, v = _stripe(Hq=2, Hkv=1, N=512, d=64, seed=5)
     od, ld = O.dense_causal(q, k, v)
     for flags in (0, O.SA_NO_QPERM, O.SA_NO_KVPERM,
-                  O.SA_NO_QPERM | O.SA_NO_KVPERM):
+                  O.SA_NO_QPERM | O.SA_NO_KVPERM, O.SA_SEGMENT_KV,
+                  O.SA_SEGMENT_KV | O.SA_NO_QPERM):
         o, lse, *_ = O.s2o_attention(q, k, v, 128, 0.0, flags)
         assert np.abs(o - od).max() < 1e-12
         assert np.abs(lse - ld).max() < 1e-12
@@ -470,6 +471,64 @@ def check_recall(O):
                   ).max() < 1e-10
 
 
+def check_segment_kv_worked(O):
+    """Segment-local key order on a hand-derived example: N = 384, S = 128,
+    every query (1, 0, ...), keys with coordinate 0 equal to 1.0 at key 10,
+    3.0 at key 100, 2.0 at key 130 and 0 elsewhere, so v_j is proportional
+    to that coordinate. Inside segment 0 the order is 100, 10, then the rest
+    by index; inside segment 1: 130, then the rest. Tiles (64 keys): A =
+    first half of segment 0 (score 4), B = second half (0), C = first half
+    of segment 1 (2), D = second half (0). L_1 = A B; L_2 = A C B D (B and
+    D tie at 0: smaller tile index first). The global order of the same
+    input puts 100, 130, 10 first instead."""
+    N, S, d = 384, 128, 8
+    qf = np.zeros((1, 1, N, d)); qf[0, 0, :, 0] = 1.0
+    kf = np.zeros((1, 1, N, d))
+    for j, a in [(10, 1.0), (100, 3.0), (130, 2.0)]:
+        kf[0, 0, j, 0] = a
+    q, k = bits(qf), bits(kf)
+    pl = O.plan(q, k, S, flags=O.SA_SEGMENT_KV)
+    seg0 = [100, 10] + [j for j in range(128) if j not in (10, 100)]
+    seg1 = [130] + [j for j in range(128, 256) if j != 130]
+    seg2 = list(range(256, 384))
+    assert pl.pi_k[0, 0].tolist() == seg0 + seg1 + seg2
+    A, B, C, D = seg0[:64], seg0[64:], seg1[:64], seg1[64:]
+    assert O.restricted_list(pl, 0, 0, 1).tolist() == A + B
+    assert O.restricted_list(pl, 0, 0, 2).tolist() == A + C + B + D
+    g = O.plan(q, k, S)
+    assert g.pi_k[0, 0, :3].tolist() == [100, 130, 10]
+
+
+def check_segment_kv_invariants(O):
+    """On stripe inputs: pi_K permutes each segment and orders it by v
+    descending (ties by index); every L_t is a concatenation of 64-key
+    chunks of pi_K[0 : t S] (each chunk once) with non-increasing sums of
+    v; SA_NO_KVPERM still gives the identity order."""
+    q, k, v = _stripe(Hq=4, Hkv=2, N=1024, d=32, seed=12)
+    S = 256
+    pl = O.plan(q, k, S, flags=O.SA_SEGMENT_KV)
+    for g in range(2):
+        pk, vs = pl.pi_k[0, g], pl.key_score[0, g]
+        for u in range(1024 // S):
+            seg = pk[u * S:(u + 1) * S]
+            assert sorted(seg.tolist()) == list(range(u * S, (u + 1) * S))
+            for a_, b_ in zip(seg[:-1], seg[1:]):
+                assert vs[a_] > vs[b_] or (vs[a_] == vs[b_] and a_ < b_)
+        chunks = {tuple(pk[i:i + 64].tolist()): i // 64
+                  for i in range(0, 1024, 64)}
+        for t in range(1, 1024 // S):
+            Lt = O.restricted_list(pl, 0, g, t)
+            tiles = [tuple(Lt[i:i + 64].tolist()) for i in range(0, len(Lt), 64)]
+            ids = [chunks[x] for x in tiles]
+            assert sorted(ids) == list(range(t * S // 64))
+            sums = [int(vs[list(x)].sum()) for x in tiles]
+            for i in range(len(sums) - 1):
+                assert sums[i] > sums[i + 1] or (
+                    sums[i] == sums[i + 1] and ids[i] < ids[i + 1])
+    pid = O.plan(q, k, S, flags=O.SA_SEGMENT_KV | O.SA_NO_KVPERM)
+    assert np.array_equal(pid.pi_k[0, 0], np.arange(1024))
+
+
 ALL_CHECKS = [
     check_fixed_point, check_dense_vs_sdpa, check_dense_closed_forms,
     check_worked_orders, check_stripe_score_bruteforce, check_plan_invariants,
@@ -478,4 +537,5 @@ ALL_CHECKS = [
     check_constant_keys_closed_form, check_strict_stop,
     check_two_level_closed_form, check_permuted_block_closed_form,
     check_monotone_tau, check_local_only, check_recall,
+    check_segment_kv_worked, check_segment_kv_invariants,
 ]

@@ -8,7 +8,8 @@ import numpy as np
 import pytest
 
 import oracle as O
-from synthetic import StripeSpec, get_config, make_stripe_inputs
+from synthetic import (StripeSpec, get_config, make_stripe_inputs,
+                       round_to_bf16_bits)
 from tests.gpu_helpers import (assert_outputs_close, assert_plan_equal,
                                run_gpu, say, stop_mismatches)
 
@@ -40,6 +41,15 @@ CASES = [
      O.SA_LOCAL_ONLY),
     ("local_only_no_earlystop", _spec(1, 2, 1, 640, 33), 128, (0.0,),
      O.SA_LOCAL_ONLY | O.SA_NO_EARLYSTOP),
+    ("segment_kv", _spec(1, 4, 2, 1024, 35), 256, (0.0, 0.05, 0.2),
+     O.SA_SEGMENT_KV),
+    ("segment_kv_s64", _spec(1, 2, 1, 768, 36), 64, (0.1, 0.4),
+     O.SA_SEGMENT_KV),
+    ("segment_kv_no_qperm", _spec(1, 2, 1, 1024, 37), 256, (0.05,),
+     O.SA_SEGMENT_KV | O.SA_NO_QPERM),
+    ("segment_kv_t64_n16384", _spec(1, 1, 1, 16384, 38, n_vert=32,
+                                    window=128), 256, (0.05,),
+     O.SA_SEGMENT_KV),
     ("s4096_merge_sort_n8192", _spec(1, 2, 1, 8192, 30, n_vert=64,
                                      window=128), 4096, (0.02,), 0),
 ]
@@ -109,6 +119,39 @@ def test_recall_from_lse():
         assert np.abs(r_gpu - r_ref).max() <= 5e-3, np.abs(r_gpu - r_ref).max()
         if flags == 0 and tau > 0.1:
             assert r_ref.mean() < 1.0 - 1e-6  # something was skipped
+
+
+def test_segment_kv_worked_example():
+    """The hand-derived segment-local example on the GPU plan (head
+    dimension zero-padded to 128): N = 384, S = 128, every query
+    (1, 0, ...), key coordinate 0 = 1.0 at key 10, 3.0 at key 100, 2.0 at
+    key 130. Segment orders 100, 10, rest / 130, rest; tiles A, B (segment
+    0, scores 4 and 0), C, D (segment 1, scores 2 and 0); L_1 = A B and
+    L_2 = A C B D. Injecting a KV order into such a plan is refused."""
+    import permuted_block_sparse_amd as pbs
+    N, S = 384, 128
+    qf = np.zeros((1, 1, N, 128), np.float32)
+    qf[0, 0, :, 0] = 1.0
+    kf = np.zeros((1, 1, N, 128), np.float32)
+    for j, a in [(10, 1.0), (100, 3.0), (130, 2.0)]:
+        kf[0, 0, j, 0] = a
+    q, k = round_to_bf16_bits(qf), round_to_bf16_bits(kf)
+    say("[segment_kv] worked example")
+    g = run_gpu(q, k, np.zeros_like(q), S, 0.0, O.SA_SEGMENT_KV)
+    seg0 = [100, 10] + [j for j in range(128) if j not in (10, 100)]
+    seg1 = [130] + [j for j in range(128, 256) if j != 130]
+    assert g["pi_k"][0, 0].tolist() == seg0 + seg1 + list(range(256, 384))
+    A, B, C, D = seg0[:64], seg0[64:], seg1[:64], seg1[64:]
+    L = g["L"][0, 0]
+    assert L[:128].tolist() == A + B
+    assert L[128:384].tolist() == A + C + B + D
+    with pytest.raises(pbs.SparseAttnError):
+        g["plan"].set_kv_order(torch_arange_order(N))
+
+
+def torch_arange_order(N):
+    import torch
+    return torch.arange(N, dtype=torch.int32, device="cuda:0").view(1, 1, N)
 
 
 def test_deterministic():

@@ -14,6 +14,14 @@ SRC = pathlib.Path(S2O.__file__).read_text()
 
 # (name, exact text in oracle/s2o.py, replacement)
 MUTANTS = [
+    ("segkv_tile_tie_desc", "Lt = tiles[np.lexsort((tid, -tscore))].reshape(-1)",
+     "Lt = tiles[np.lexsort((-tid, -tscore))].reshape(-1)"),
+    ("segkv_tiles_ascending", "Lt = tiles[np.lexsort((tid, -tscore))].reshape(-1)",
+     "Lt = tiles[np.lexsort((tid, tscore))].reshape(-1)"),
+    ("segkv_score_first_key", "tscore = v[tiles].sum(axis=1)",
+     "tscore = v[tiles[:, 0]]"),
+    ("segkv_keys_ascending", "seg[np.lexsort((seg, -v[seg]))]",
+     "seg[np.lexsort((seg, v[seg]))]"),
     ("local_only_ignored", "    if pl.flags & SA_LOCAL_ONLY:\n", "    if False:\n"),
     ("recall_strict_causal", "causal = j[None, :] <= rows[:, None]",
      "causal = j[None, :] < rows[:, None]"),

@@ -308,6 +308,40 @@ def extras(args, cfg, q, k, v, tq, tk, tv, pl, out, S, tau, timed):
     log(f"[bench] local window only: {res['local_window_only']}")
     del pl_loc, o_loc, lse_loc
 
+    # fixed tile budget at matched sparsity: the smallest K whose visited
+    # tiles (min(K, t S / 64) per block) reach the tau stop's total
+    pl.set_tau(tau)
+    pbs.prefill(pl, tq, tk, tv, out=out)
+    visited_tau = int(pl.n_I().sum())
+    bps = S // 64
+    caps = np.repeat(np.arange(T) * bps, B * Hq * bps)
+    lo_k, hi_k = 0, int(caps.max())
+    while lo_k < hi_k:
+        mid = (lo_k + hi_k) // 2
+        if int(np.minimum(caps, mid).sum()) >= visited_tau:
+            hi_k = mid
+        else:
+            lo_k = mid + 1
+    K = lo_k
+    pl.set_budget(K)
+    o_b = torch.empty_like(tq)
+    b_ms, _ = timed(lambda: pbs.prefill(pl, tq, tk, tv, out=o_b), 3)
+    _, lse_b = pbs.prefill(pl, tq, tk, tv, out=o_b, return_lse=True)
+    n_b = pl.n_I()
+    pl.set_budget(-1)
+    sel = B * Hq * T * S * (S + 1) / 2 + 4096.0 * n_b.sum()
+    diff = (o_b.float() - dense.float())
+    res["fixed_budget_matched"] = {
+        "budget_tiles": K, "visited_tiles": int(n_b.sum()),
+        "tau_visited_tiles": visited_tau,
+        "prefill_ms": round(b_ms, 4),
+        "pair_sparsity": round(float(1.0 - sel / (B * Hq * N * (N + 1) / 2)),
+                               5),
+        "mse_vs_dense": float((diff * diff).mean().item()),
+        **recall_stats(lse_b)}
+    log(f"[bench] fixed budget (matched): {res['fixed_budget_matched']}")
+    del o_b, lse_b
+
     # segment-local key order (the PBS-Attn variant) at the same tau
     plan_seg_ms, _ = timed(
         lambda: pbs.plan(tq, tk, S, tau, flags=pbs.SA_SEGMENT_KV), 3)

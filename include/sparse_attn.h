@@ -159,6 +159,14 @@ int sparse_attn_prefill(const sa_plan* plan, const void* q, const void* k,
  * on tau). Returns SA_ERR_INVALID_ARG for tau < 0 or NaN. */
 int sparse_attn_plan_set_tau(sa_plan* plan, double tau);
 
+/* Fixed tile budget instead of the tau stop: with tiles >= 0 every query
+ * block of segment t visits the first min(tiles, t S / 64) tiles of L_t
+ * (the most important tiles of the mean-pooled ranking, the same count for
+ * every block -- the fixed-budget selection the S2O page compares its
+ * adaptive stop with, Key points); tiles < 0 restores the tau stop (the
+ * default). n_I records the count. SA_LOCAL_ONLY still visits no tile. */
+int sparse_attn_plan_set_budget(sa_plan* plan, int32_t tiles);
+
 /* What sparse_attn_plan_export copies (element type, count). */
 #define SA_EXPORT_PI_K         0  /* int32 [B, Hkv, N]                        */
 #define SA_EXPORT_PI_Q         1  /* int32 [B, Hq, N]                         */

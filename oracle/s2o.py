@@ -344,7 +344,8 @@ def block_stop(qbar: np.ndarray, rows: np.ndarray, t: int,
 
 
 def stop_points(q_bits, k_bits, pl: Plan, tau: float,
-                blocks: Optional[Sequence[Tuple[int, int, int]]] = None):
+                blocks: Optional[Sequence[Tuple[int, int, int]]] = None,
+                budget: Optional[int] = None):
     """n_I for every query block (or the listed (b, h, I) blocks).
 
     Returns (n_I [B, Hq, N/64] int64 with -1 for blocks not computed,
@@ -353,6 +354,12 @@ def stop_points(q_bits, k_bits, pl: Plan, tau: float,
     SA_LOCAL_ONLY: no tile of L_t is visited (n_I = 0, empty traces) -- the
     "dense local window only" baseline of the S2O page's component ablation
     (Key points).
+
+    ``budget`` >= 0: a fixed tile budget replaces the stop test; every block
+    of segment t visits the first min(budget, t S / 64) tiles of L_t (the
+    most important tiles of the mean-pooled ranking, the same count for
+    every block -- the fixed-budget selection the S2O page's adaptive stop
+    is compared with, Key points). SA_LOCAL_ONLY takes precedence.
     """
     B, Hq, N, d = q_bits.shape
     G = Hq // pl.heads_kv
@@ -369,6 +376,12 @@ def stop_points(q_bits, k_bits, pl: Plan, tau: float,
     if pl.flags & SA_LOCAL_ONLY:
         for b, h, I in blocks:
             n_I[b, h, I] = 0
+            traces[(b, h, I)] = np.zeros(0)
+        return n_I, traces
+    if budget is not None and budget >= 0:
+        for b, h, I in blocks:
+            t = (I * BLOCK) // S
+            n_I[b, h, I] = min(budget, t * S // BLOCK)
             traces[(b, h, I)] = np.zeros(0)
         return n_I, traces
     by_group: Dict[Tuple[int, int, int], list] = {}

@@ -103,6 +103,13 @@ class SparsePlan:
                    "sparse_attn_plan_set_tau")
         self.params.tau = float(tau)
 
+    def set_budget(self, tiles: int) -> None:
+        """Fixed tile budget per query block instead of the tau stop
+        (tiles < 0: back to the tau stop)."""
+        _lib.check(_lib.load().sparse_attn_plan_set_budget(self._handle,
+                                                           int(tiles)),
+                   "sparse_attn_plan_set_budget")
+
     def set_kv_order(self, pi_k: torch.Tensor, stream=None) -> None:
         if pi_k.dtype != torch.int32 or not pi_k.is_cuda:
             raise TypeError("pi_k must be an int32 CUDA tensor")

@@ -373,7 +373,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_fwd(AttnArgs a) {
 #pragma unroll
   for (int w = 0; w < kWaves; ++w) wgmax = max(wgmax, wave_maxrow[w]);
   const int ndiag = min(max((wgmax - seg0) / kBlock + 1, 1), bps);
-  const int ntiles = a.local_only ? 0 : t * bps;
+  const int ntiles = a.local_only ? 0
+                     : a.budget >= 0 ? min(t * bps, a.budget)
+                                     : t * bps;
   const int nsteps = ndiag + ntiles;
   const int32_t* Lt =
       a.L + (size_t)bg * a.list_len + (size_t)a.S * t * (t - 1) / 2;

@@ -77,6 +77,7 @@ struct AttnArgs {
   double kappa;
   float c2;  // kappa * log2(e)
   int local_only;  // 1: no tile of L_t is visited (dense local window only)
+  int budget;      // >= 0: at most this many tiles of L_t (tau is then 0)
 };
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
 

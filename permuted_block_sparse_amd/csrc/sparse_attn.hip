@@ -101,6 +101,7 @@ Layout layout_of(const PlanDims& d) {
 
 struct sa_plan {
   sa_params p;
+  int32_t budget = -1;  // >= 0: fixed tile budget instead of the tau stop
   PlanDims d;
   Layout lay;
   char* ws;
@@ -261,11 +262,21 @@ int sparse_attn_prefill(const sa_plan* plan, const void* q, const void* k,
   const int qblocks = d.G * (d.S / kBlock);
   a.wg_per_group = (qblocks + 3) / 4;
   a.n_groups = d.B * d.Hkv * d.T;
-  a.tau = (plan->p.flags & SA_NO_EARLYSTOP) ? 0.0 : plan->p.tau;
+  // a fixed budget replaces the stop test (tau = 0: no estimate stops)
+  a.tau = (plan->p.flags & SA_NO_EARLYSTOP) || plan->budget >= 0
+              ? 0.0
+              : plan->p.tau;
   a.local_only = (plan->p.flags & SA_LOCAL_ONLY) ? 1 : 0;
+  a.budget = plan->budget;
   a.kappa = 1.0 / std::sqrt((double)kHeadDim);
   a.c2 = (float)(a.kappa * 1.4426950408889634074);
   return hip_status(launch_attention(a, stream));
+}
+
+int sparse_attn_plan_set_budget(sa_plan* plan, int32_t tiles) {
+  if (plan == nullptr) return SA_ERR_NULL_POINTER;
+  plan->budget = tiles < 0 ? -1 : tiles;
+  return SA_OK;
 }
 
 int sparse_attn_plan_set_tau(sa_plan* plan, double tau) {

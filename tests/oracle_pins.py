@@ -529,6 +529,33 @@ def check_segment_kv_invariants(O):
     assert np.array_equal(pid.pi_k[0, 0], np.arange(1024))
 
 
+def check_budget(O):
+    """Fixed tile budget: n_I = min(K, t S / 64) in segment t (closed
+    form); K = 0 gives the dense-local-window-only outputs; a budget of
+    every tile gives dense attention; matched visits differ from the tau
+    stop's per-block counts (the budget is the same for every block)."""
+    q, k, v = _stripe(Hq=2, Hkv=1, N=512, d=32, seed=13)
+    S = 128
+    pl = O.plan(q, k, S)
+    for K in (0, 1, 3, 100):
+        n_I, _ = O.stop_points(q, k, pl, 0.7, budget=K)
+        for I in range(512 // 64):
+            t = I * 64 // S
+            assert (n_I[0, :, I] == min(K, t * S // 64)).all()
+    n0, _ = O.stop_points(q, k, pl, 0.3, budget=0)
+    o0, l0 = O.attend(q, k, v, pl, n0)
+    pll = O.plan(q, k, S, flags=O.SA_LOCAL_ONLY)
+    nl, _ = O.stop_points(q, k, pll, 0.3)
+    ol, ll = O.attend(q, k, v, pll, nl)
+    assert np.abs(o0 - ol).max() < 1e-12 and np.abs(l0 - ll).max() < 1e-12
+    nall, _ = O.stop_points(q, k, pl, 0.9, budget=512 // 64)
+    oall, _ = O.attend(q, k, v, pl, nall)
+    od, _ = O.dense_causal(q, k, v)
+    assert np.abs(oall - od).max() < 1e-12
+    nb, _ = O.stop_points(q, k, pll, 0.0, budget=5)
+    assert (nb == 0).all()  # SA_LOCAL_ONLY takes precedence
+
+
 ALL_CHECKS = [
     check_fixed_point, check_dense_vs_sdpa, check_dense_closed_forms,
     check_worked_orders, check_stripe_score_bruteforce, check_plan_invariants,
@@ -537,5 +564,5 @@ ALL_CHECKS = [
     check_constant_keys_closed_form, check_strict_stop,
     check_two_level_closed_form, check_permuted_block_closed_form,
     check_monotone_tau, check_local_only, check_recall,
-    check_segment_kv_worked, check_segment_kv_invariants,
+    check_segment_kv_worked, check_segment_kv_invariants, check_budget,
 ]

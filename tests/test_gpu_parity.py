@@ -154,6 +154,27 @@ def torch_arange_order(N):
     return torch.arange(N, dtype=torch.int32, device="cuda:0").view(1, 1, N)
 
 
+def test_budget_parity():
+    """Fixed tile budget instead of the tau stop: n_I = min(K, t S / 64)
+    exactly, outputs against the oracle on those stop points; a negative
+    budget restores the tau stop."""
+    spec = _spec(1, 4, 2, 1024, 39)
+    q, k, v = make_stripe_inputs(spec)
+    S = 256
+    pl = O.plan(q, k, S)
+    for K in (0, 2, 7):
+        say(f"[budget] K={K}")
+        g = run_gpu(q, k, v, S, 0.05, budget=K)
+        n_ref, _ = O.stop_points(q, k, pl, 0.05, budget=K)
+        assert np.array_equal(g["n_I"], n_ref)
+        o_ref, l_ref = O.attend(q, k, v, pl, n_ref)
+        assert_outputs_close(g["o"], o_ref, g["lse"], l_ref)
+    say("[budget] back to the tau stop")
+    g = run_gpu(q, k, v, S, 0.05, budget=-1)
+    n_tau, traces = O.stop_points(q, k, pl, 0.05)
+    assert not stop_mismatches(g["n_I"], n_tau, traces, 0.05)
+
+
 def test_deterministic():
     spec = _spec(1, 4, 1, 2048, 32)
     q, k, v = make_stripe_inputs(spec)

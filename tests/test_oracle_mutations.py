@@ -14,6 +14,10 @@ SRC = pathlib.Path(S2O.__file__).read_text()
 
 # (name, exact text in oracle/s2o.py, replacement)
 MUTANTS = [
+    ("budget_off_by_one", "n_I[b, h, I] = min(budget, t * S // BLOCK)",
+     "n_I[b, h, I] = min(budget + 1, t * S // BLOCK)"),
+    ("budget_ignores_segment", "n_I[b, h, I] = min(budget, t * S // BLOCK)",
+     "n_I[b, h, I] = budget"),
     ("segkv_tile_tie_desc", "Lt = tiles[np.lexsort((tid, -tscore))].reshape(-1)",
      "Lt = tiles[np.lexsort((-tid, -tscore))].reshape(-1)"),
     ("segkv_tiles_ascending", "Lt = tiles[np.lexsort((tid, -tscore))].reshape(-1)",

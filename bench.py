@@ -342,6 +342,44 @@ def extras(args, cfg, q, k, v, tq, tk, tv, pl, out, S, tau, timed):
     log(f"[bench] fixed budget (matched): {res['fixed_budget_matched']}")
     del o_b, lse_b
 
+    # exact per-block max test (the BSFA variant): every tile scored
+    # exactly; the threshold is bisected until the attended tiles match the
+    # tau stop's visited tiles
+    def exact_count(theta):
+        pl.set_max_threshold(theta)
+        pbs.prefill(pl, tq, tk, tv, out=out)
+        return int(pl.n_I().sum())
+    lo_t, hi_t = 0.0, 4.0
+    while exact_count(hi_t) > visited_tau:
+        hi_t *= 2.0
+    while exact_count(lo_t) < visited_tau:
+        lo_t -= 4.0
+    for _ in range(16):
+        mid = 0.5 * (lo_t + hi_t)
+        if exact_count(mid) >= visited_tau:
+            lo_t = mid
+        else:
+            hi_t = mid
+    pl.set_max_threshold(lo_t)
+    o_x = torch.empty_like(tq)
+    x_ms, _ = timed(lambda: pbs.prefill(pl, tq, tk, tv, out=o_x), 3)
+    _, lse_x = pbs.prefill(pl, tq, tk, tv, out=o_x, return_lse=True)
+    n_x = pl.n_I()
+    pl.set_max_threshold(float("nan"))
+    sel = B * Hq * T * S * (S + 1) / 2 + 4096.0 * n_x.sum()
+    diff = (o_x.float() - dense.float())
+    res["exact_max_matched"] = {
+        "theta": round(lo_t, 5), "attended_tiles": int(n_x.sum()),
+        "scored_tiles": int(sum(B * Hq * bps * t * bps for t in range(T))),
+        "tau_visited_tiles": visited_tau,
+        "prefill_ms": round(x_ms, 4),
+        "pair_sparsity": round(float(1.0 - sel / (B * Hq * N * (N + 1) / 2)),
+                               5),
+        "mse_vs_dense": float((diff * diff).mean().item()),
+        **recall_stats(lse_x)}
+    log(f"[bench] exact max test (matched): {res['exact_max_matched']}")
+    del o_x, lse_x
+
     # segment-local key order (the PBS-Attn variant) at the same tau
     plan_seg_ms, _ = timed(
         lambda: pbs.plan(tq, tk, S, tau, flags=pbs.SA_SEGMENT_KV), 3)

@@ -167,6 +167,17 @@ int sparse_attn_plan_set_tau(sa_plan* plan, double tau);
  * default). n_I records the count. SA_LOCAL_ONLY still visits no tile. */
 int sparse_attn_plan_set_budget(sa_plan* plan, int32_t tiles);
 
+/* Exact per-block maximum test instead of the tau stop (the BSFA page,
+ * abstract: exact query-key scores, a block is skipped when its maximum
+ * score is under a threshold; the page calibrates one per layer and head,
+ * here it is given). With theta not NaN every tile of L_t is scored
+ * exactly and attended iff max over its 64 x 64 logits kappa q . k >= theta
+ * (+inf: none, -inf: all); the dense local window is always attended and
+ * n_I counts the attended tiles. theta = NaN (the default) restores the tau
+ * stop. Takes precedence over a budget; SA_LOCAL_ONLY still visits no
+ * tile. */
+int sparse_attn_plan_set_max_threshold(sa_plan* plan, double theta);
+
 /* What sparse_attn_plan_export copies (element type, count). */
 #define SA_EXPORT_PI_K         0  /* int32 [B, Hkv, N]                        */
 #define SA_EXPORT_PI_Q         1  /* int32 [B, Hq, N]                         */

@@ -26,18 +26,23 @@ Pinned parts (see tests/test_oracle_*.py):
     logsumexp difference of the selected and the full causal key sets
     (library logsumexp), and to the own-segment share for SA_LOCAL_ONLY;
   * the segment-local key order (SA_SEGMENT_KV) -- a hand-derived example
-    of the tile order, invariants, and tau = 0 reproducing dense attention.
+    of the tile order, invariants, and tau = 0 reproducing dense attention;
+  * the exact per-block maximum test -- tile maxima by brute force (library
+    einsum), theta = -inf / +inf reproducing dense / local-only attention,
+    monotone selection in theta.
 Parity unpinned: the agreement of the sparsity/MSE figures with the numbers
 printed on the S2O summary page (those need real models and datasets).
 """
 from .s2o import (SA_NO_QPERM, SA_NO_KVPERM, SA_NO_EARLYSTOP, SA_LOCAL_ONLY,
                   SA_SEGMENT_KV,
                   Plan, decode_bf16, fixed_point, dense_causal, plan,
-                  stop_points, attend, recall, s2o_attention,
+                  stop_points, attend, recall, exact_max_selection,
+                  s2o_attention,
                   selected_counts, metrics, restricted_list, kappa_of)
 
 __all__ = ["SA_NO_QPERM", "SA_NO_KVPERM", "SA_NO_EARLYSTOP", "SA_LOCAL_ONLY",
            "SA_SEGMENT_KV",
            "Plan", "decode_bf16", "fixed_point", "dense_causal", "plan",
-           "stop_points", "attend", "recall", "s2o_attention",
+           "stop_points", "attend", "recall", "exact_max_selection",
+           "s2o_attention",
            "selected_counts", "metrics", "restricted_list", "kappa_of"]

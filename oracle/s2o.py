@@ -412,7 +412,8 @@ def stop_points(q_bits, k_bits, pl: Plan, tau: float,
 # --------------------------------------------------------------------------
 
 def attend(q_bits, k_bits, v_bits, pl: Plan, n_I: np.ndarray,
-           blocks: Optional[Sequence[Tuple[int, int, int]]] = None):
+           blocks: Optional[Sequence[Tuple[int, int, int]]] = None,
+           tile_mask: Optional[Dict[Tuple[int, int, int], np.ndarray]] = None):
     """Softmax attention of each query over its selected key set, float64.
 
     For query block I in segment t with stop point n_I, row i attends to
@@ -422,7 +423,9 @@ def attend(q_bits, k_bits, v_bits, pl: Plan, n_I: np.ndarray,
     the PBS-Attn page; scale as in AB-Sparse Eq. (1)). The result is written
     back to the query's original row: no tensor is moved (S2O summary,
     Summary). Returns (o [B, Hq, N, d], lse [B, Hq, N]) with NaN in rows of
-    blocks not computed.
+    blocks not computed. ``tile_mask`` ((b, h, I) -> bool per tile of L_t)
+    selects an arbitrary subset of the tiles instead of the first n_I (the
+    exact per-block max test).
     """
     B, Hq, N, d = q_bits.shape
     G = Hq // pl.heads_kv
@@ -447,8 +450,12 @@ def attend(q_bits, k_bits, v_bits, pl: Plan, n_I: np.ndarray,
             t = (I * BLOCK) // S
             local = np.arange(t * S, (t + 1) * S)
             n = int(n_I[b, h, I])
-            far = (restricted_list(pl, b, g, t)[:n * BLOCK] if t > 0
-                   else np.zeros(0, dtype=np.int64))
+            if tile_mask is not None and t > 0:
+                tiles = restricted_list(pl, b, g, t).reshape(-1, BLOCK)
+                far = tiles[np.asarray(tile_mask[(b, h, I)], bool)].reshape(-1)
+            else:
+                far = (restricted_list(pl, b, g, t)[:n * BLOCK] if t > 0
+                       else np.zeros(0, dtype=np.int64))
             keys = np.concatenate([local, far])
             z = kap * (q[rows] @ k[keys].T)
             z[:, :S][local[None, :] > rows[:, None]] = -np.inf
@@ -458,6 +465,49 @@ def attend(q_bits, k_bits, v_bits, pl: Plan, n_I: np.ndarray,
             o[b, h, rows] = (p @ v[keys]) / s
             lse[b, h, rows] = (m + np.log(s))[:, 0]
     return o, lse
+
+
+def exact_max_selection(q_bits, k_bits, pl: Plan, theta: float,
+                        blocks: Optional[Sequence[Tuple[int, int, int]]] = None):
+    """The exact per-block maximum test of the BSFA page (abstract): every
+    tile of L_t is scored exactly and attended only if the largest scaled
+    logit of the 64 x 64 tile, max over its query rows i and keys j of
+    kappa q_i . k_j, is at least theta (a given threshold; the page
+    calibrates one per layer and head on data). READING: no early stop in
+    this mode, the dense local window is always attended, and an absolute
+    threshold makes the selection independent of the visiting order.
+    Returns (counts n_I [B, Hq, N/64], masks (b, h, I) -> bool per tile,
+    maxima (b, h, I) -> tile maxima).
+    """
+    B, Hq, N, d = q_bits.shape
+    G = Hq // pl.heads_kv
+    S = pl.segment
+    kap = kappa_of(d)
+    nb = N // BLOCK
+    n_I = np.full((B, Hq, nb), -1, dtype=np.int64)
+    masks, maxima = {}, {}
+    if blocks is None:
+        blocks = [(b, h, I) for b in range(B) for h in range(Hq)
+                  for I in range(nb)]
+    for b, h, I in blocks:
+        g = h // G
+        t = (I * BLOCK) // S
+        if t == 0 or pl.flags & SA_LOCAL_ONLY:
+            n_I[b, h, I] = 0
+            masks[(b, h, I)] = np.zeros(t * S // BLOCK, dtype=bool)
+            maxima[(b, h, I)] = np.zeros(0)
+            continue
+        q = decode_bf16(q_bits[b, h])
+        k = decode_bf16(k_bits[b, g])
+        rows = pl.pi_q[b, h, I * BLOCK:(I + 1) * BLOCK]
+        tiles = restricted_list(pl, b, g, t).reshape(-1, BLOCK)
+        z = kap * (q[rows] @ k[tiles.reshape(-1)].T)        # 64 x (t S)
+        mx = z.reshape(BLOCK, -1, BLOCK).max(axis=(0, 2))
+        sel = mx >= theta
+        n_I[b, h, I] = int(sel.sum())
+        masks[(b, h, I)] = sel
+        maxima[(b, h, I)] = mx
+    return n_I, masks, maxima
 
 
 def recall(q_bits, k_bits, pl: Plan, n_I: np.ndarray,

@@ -110,6 +110,12 @@ class SparsePlan:
                                                            int(tiles)),
                    "sparse_attn_plan_set_budget")
 
+    def set_max_threshold(self, theta: float) -> None:
+        """Exact per-block maximum test with threshold theta on the scaled
+        logits instead of the tau stop (NaN: back to the tau stop)."""
+        _lib.check(_lib.load().sparse_attn_plan_set_max_threshold(
+            self._handle, float(theta)), "sparse_attn_plan_set_max_threshold")
+
     def set_kv_order(self, pi_k: torch.Tensor, stream=None) -> None:
         if pi_k.dtype != torch.int32 or not pi_k.is_cuda:
             raise TypeError("pi_k must be an int32 CUDA tensor")

@@ -33,6 +33,7 @@ SA_EXPORT_POOLED = 7
 EXPORTED_SYMBOLS = (
     "sparse_attn_workspace_bytes", "sparse_attn_plan", "sparse_attn_prefill",
     "sparse_attn_plan_set_tau", "sparse_attn_plan_set_budget",
+    "sparse_attn_plan_set_max_threshold",
     "sparse_attn_plan_export_bytes",
     "sparse_attn_plan_export", "sparse_attn_plan_set_kv_order",
     "sparse_attn_plan_destroy", "sparse_attn_status_string",
@@ -79,6 +80,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.sparse_attn_plan_set_tau.restype = i32
     lib.sparse_attn_plan_set_budget.argtypes = [vp, i32]
     lib.sparse_attn_plan_set_budget.restype = i32
+    lib.sparse_attn_plan_set_max_threshold.argtypes = [vp, ctypes.c_double]
+    lib.sparse_attn_plan_set_max_threshold.restype = i32
     lib.sparse_attn_plan_export_bytes.argtypes = [vp, i32]
     lib.sparse_attn_plan_export_bytes.restype = sz
     lib.sparse_attn_plan_export.argtypes = [vp, i32, vp, sz, vp]

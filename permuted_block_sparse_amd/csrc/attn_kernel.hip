@@ -121,6 +121,19 @@ __device__ __forceinline__ float wave_sum(float x) {
                                        __builtin_bit_cast(int, x)));
 }
 
+__device__ __forceinline__ float wave_max(float x) {
+  x = fmaxf(x, __int_as_float(dpp_xor1(__float_as_int(x))));
+  x = fmaxf(x, __int_as_float(dpp_xor2(__float_as_int(x))));
+  x = fmaxf(x, __int_as_float(dpp_half_mirror(__float_as_int(x))));
+  x = fmaxf(x, __int_as_float(dpp_mirror(__float_as_int(x))));
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x),
+                                            __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  x = max_xor32(x);
+  return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(
+                                       __builtin_bit_cast(int, x)));
+}
+
 __device__ __forceinline__ int wave_sum_int(int x) {
   x += dpp_xor1(x);
   x += dpp_xor2(x);
@@ -238,6 +251,15 @@ __device__ __forceinline__ void qk_tile(const char* Kt, const bf16x8 (&qr)[8],
     sacc[0] = mfma32(op[s & 1][0], qr[s], sacc[0]);
     sacc[1] = mfma32(op[s & 1][1], qr[s], sacc[1]);
   }
+}
+
+__device__ __forceinline__ float lane_max(const f32x16 (&sacc)[2]) {
+  float v4[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) v4[r & 3] = fmaxf(v4[r & 3], sacc[kb][r]);
+  return fmaxf(fmaxf(v4[0], v4[1]), fmaxf(v4[2], v4[3]));
 }
 
 __device__ __forceinline__ float lane_sum(const f32x16 (&sacc)[2]) {
@@ -409,7 +431,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_fwd(AttnArgs a) {
   __syncthreads();
 
   bool active = valid;
-  int n_visit = t > 0 ? ntiles : 0;
+  // exact per-block max mode: n_I counts the attended tiles
+  int n_visit = a.exact ? 0 : (t > 0 ? ntiles : 0);
   for (int s = 0; s < nsteps; ++s) {
     const char* Kt = tiles[s & 1];
     const char* Vt = Kt + kTileBytes;
@@ -434,7 +457,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_fwd(AttnArgs a) {
     float ps = 0.f;
     if (compute) {
       qk_tile(Kt, qr, sacc, ra);
-      ps = wave_sum(lane_sum(sacc));
+      // the half's share of the tile statistic: its partial tile sum (mean
+      // estimate), or its tile maximum (exact per-block max mode)
+      ps = a.exact ? wave_max(lane_max(sacc)) : wave_sum(lane_sum(sacc));
       if (lane == 0)
         box[wave] = ((unsigned long long)(s + 1) << 32) | __float_as_uint(ps);
     }
@@ -472,6 +497,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_fwd(AttnArgs a) {
             const int jk = j0 + kb * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
             if (jk > iq) sacc[kb][r] = -INFINITY;
           }
+      } else if (a.exact) {
+        // exact per-block max test: attend the tile iff its largest logit
+        // reaches the threshold (both halves take max of the same two
+        // values); no stop
+        take = fmaxf(ps, po) >= a.exact_thr;
+        n_visit += take ? 1 : 0;
       } else {
         // share est / (acc + est) < tau, without the division
         const double est = kBlock * (double)ex;

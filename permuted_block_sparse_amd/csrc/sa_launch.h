@@ -78,6 +78,8 @@ struct AttnArgs {
   float c2;  // kappa * log2(e)
   int local_only;  // 1: no tile of L_t is visited (dense local window only)
   int budget;      // >= 0: at most this many tiles of L_t (tau is then 0)
+  int exact;       // 1: exact per-block max test instead of the tau stop
+  float exact_thr; // that test's threshold on the raw dot products (theta / kappa)
 };
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
 

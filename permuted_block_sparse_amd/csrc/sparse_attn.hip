@@ -6,6 +6,7 @@
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
+#include <limits>
 #include <new>
 
 #include "sa_launch.h"
@@ -102,6 +103,7 @@ Layout layout_of(const PlanDims& d) {
 struct sa_plan {
   sa_params p;
   int32_t budget = -1;  // >= 0: fixed tile budget instead of the tau stop
+  double max_theta = std::numeric_limits<double>::quiet_NaN();  // exact test
   PlanDims d;
   Layout lay;
   char* ws;
@@ -262,15 +264,26 @@ int sparse_attn_prefill(const sa_plan* plan, const void* q, const void* k,
   const int qblocks = d.G * (d.S / kBlock);
   a.wg_per_group = (qblocks + 3) / 4;
   a.n_groups = d.B * d.Hkv * d.T;
-  // a fixed budget replaces the stop test (tau = 0: no estimate stops)
-  a.tau = (plan->p.flags & SA_NO_EARLYSTOP) || plan->budget >= 0
+  // a fixed budget or the exact max test replaces the stop test (tau = 0:
+  // no estimate stops); the exact test takes precedence over a budget
+  a.exact = std::isnan(plan->max_theta) ? 0 : 1;
+  a.tau = (plan->p.flags & SA_NO_EARLYSTOP) || plan->budget >= 0 || a.exact
               ? 0.0
               : plan->p.tau;
   a.local_only = (plan->p.flags & SA_LOCAL_ONLY) ? 1 : 0;
-  a.budget = plan->budget;
+  a.budget = a.exact ? -1 : plan->budget;
+  a.exact_thr = a.exact ? (float)(plan->max_theta *
+                                  std::sqrt((double)kHeadDim))
+                        : 0.f;
   a.kappa = 1.0 / std::sqrt((double)kHeadDim);
   a.c2 = (float)(a.kappa * 1.4426950408889634074);
   return hip_status(launch_attention(a, stream));
+}
+
+int sparse_attn_plan_set_max_threshold(sa_plan* plan, double theta) {
+  if (plan == nullptr) return SA_ERR_NULL_POINTER;
+  plan->max_theta = theta;
+  return SA_OK;
 }
 
 int sparse_attn_plan_set_budget(sa_plan* plan, int32_t tiles) {

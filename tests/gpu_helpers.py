@@ -36,13 +36,16 @@ def bf16_tensor_to_f64(t):
         np.float64)
 
 
-def run_gpu(q, k, v, segment, tau, flags=0, kv_order=None, budget=None):
+def run_gpu(q, k, v, segment, tau, flags=0, kv_order=None, budget=None,
+            max_theta=None):
     import torch
     import permuted_block_sparse_amd as pbs
     tq, tk, tv = to_device(q), to_device(k), to_device(v)
     pl = pbs.plan(tq, tk, segment, tau, flags=flags)
     if budget is not None:
         pl.set_budget(budget)
+    if max_theta is not None:
+        pl.set_max_threshold(max_theta)
     if kv_order is not None:
         pl.set_kv_order(torch.from_numpy(
             np.ascontiguousarray(kv_order, dtype=np.int32)).to("cuda:0"))

@@ -556,6 +556,47 @@ def check_budget(O):
     assert (nb == 0).all()  # SA_LOCAL_ONLY takes precedence
 
 
+def check_exact_max(O):
+    """Exact per-block maximum test: tile maxima by brute force (library
+    einsum over the explicit tile keys), selection = maxima >= theta;
+    theta = -inf gives dense attention, theta = +inf the dense local window
+    only; the selected set shrinks as theta grows."""
+    q, k, v = _stripe(Hq=2, Hkv=1, N=512, d=32, seed=14)
+    S, d = 128, 32
+    pl = O.plan(q, k, S)
+    tq = torch.from_numpy(O.decode_bf16(q))
+    tk = torch.from_numpy(O.decode_bf16(k))
+    _, _, mx = O.exact_max_selection(q, k, pl, 0.0)
+    for (b, h, I), m in mx.items():
+        t = I * 64 // S
+        if t == 0:
+            continue
+        rows = torch.from_numpy(pl.pi_q[b, h, I * 64:(I + 1) * 64])
+        tiles = O.restricted_list(pl, b, 0, t).reshape(-1, 64)
+        for c in range(tiles.shape[0]):
+            keys = torch.from_numpy(tiles[c])
+            z = torch.einsum("id,jd->ij", tq[b, h][rows], tk[b, 0][keys])
+            assert abs(float(z.amax()) / math.sqrt(d) - m[c]) < 1e-12
+    vals = np.concatenate([m for m in mx.values() if len(m)])
+    theta = float(np.sort(vals)[len(vals) // 2])  # an attained maximum
+    n_I, masks, _ = O.exact_max_selection(q, k, pl, theta)
+    for key, m in mx.items():
+        assert np.array_equal(masks[key], m >= theta)
+        assert n_I[key] == int((m >= theta).sum())
+    od, _ = O.dense_causal(q, k, v)
+    n_all, m_all, _ = O.exact_max_selection(q, k, pl, -np.inf)
+    o_all, _ = O.attend(q, k, v, pl, n_all, tile_mask=m_all)
+    assert np.abs(o_all - od).max() < 1e-12
+    n_no, m_no, _ = O.exact_max_selection(q, k, pl, np.inf)
+    o_no, _ = O.attend(q, k, v, pl, n_no, tile_mask=m_no)
+    pll = O.plan(q, k, S, flags=O.SA_LOCAL_ONLY)
+    nl, _ = O.stop_points(q, k, pll, 0.0)
+    ol, _ = O.attend(q, k, v, pll, nl)
+    assert np.abs(o_no - ol).max() < 1e-12
+    hi, _, _ = O.exact_max_selection(q, k, pl, theta + 0.5)
+    assert (hi <= n_I).all() and hi.sum() < n_I.sum()
+
+
 ALL_CHECKS = [
     check_fixed_point, check_dense_vs_sdpa, check_dense_closed_forms,
     check_worked_orders, check_stripe_score_bruteforce, check_plan_invariants,
@@ -565,4 +606,5 @@ ALL_CHECKS = [
     check_two_level_closed_form, check_permuted_block_closed_form,
     check_monotone_tau, check_local_only, check_recall,
     check_segment_kv_worked, check_segment_kv_invariants, check_budget,
+    check_exact_max,
 ]

@@ -25,7 +25,7 @@ def declared_functions():
 def test_every_declared_symbol_is_exported():
     lib = _lib.load()
     names = declared_functions()
-    assert len(names) == 10
+    assert len(names) == 11
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(_lib.EXPORTED_SYMBOLS)

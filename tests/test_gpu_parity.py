@@ -175,6 +175,45 @@ def test_budget_parity():
     assert not stop_mismatches(g["n_I"], n_tau, traces, 0.05)
 
 
+def test_exact_max_parity():
+    """Exact per-block maximum test: attended-tile counts equal the
+    oracle's and outputs match the oracle on its tile masks, at thresholds
+    placed in gaps of at least 2e-3 between the oracle's tile maxima (fp32
+    against float64 maxima cannot disagree there); theta = -inf gives dense
+    attention, +inf the local window only, NaN restores the tau stop."""
+    spec = _spec(1, 4, 2, 1024, 40)
+    q, k, v = make_stripe_inputs(spec)
+    S = 256
+    pl = O.plan(q, k, S)
+    _, _, mx = O.exact_max_selection(q, k, pl, 0.0)
+    vals = np.sort(np.concatenate([m for m in mx.values() if len(m)]))
+    gaps = np.flatnonzero(np.diff(vals) >= 2e-3)
+    for frac in (0.3, 0.7):
+        i = gaps[np.searchsorted(gaps, int(frac * len(vals)))]
+        theta = float((vals[i] + vals[i + 1]) / 2)
+        say(f"[exact] theta={theta:.4f}")
+        g = run_gpu(q, k, v, S, 0.05, max_theta=theta)
+        n_ref, masks, _ = O.exact_max_selection(q, k, pl, theta)
+        assert np.array_equal(g["n_I"], n_ref)
+        o_ref, l_ref = O.attend(q, k, v, pl, n_ref, tile_mask=masks)
+        assert_outputs_close(g["o"], o_ref, g["lse"], l_ref)
+    od, ld = O.dense_causal(q, k, v)
+    say("[exact] theta=-inf")
+    g = run_gpu(q, k, v, S, 0.05, max_theta=-np.inf)
+    assert_outputs_close(g["o"], od, g["lse"], ld)
+    say("[exact] theta=+inf")
+    g = run_gpu(q, k, v, S, 0.05, max_theta=np.inf)
+    assert (g["n_I"] == 0).all()
+    pll = O.plan(q, k, S, flags=O.SA_LOCAL_ONLY)
+    nl, _ = O.stop_points(q, k, pll, 0.0)
+    ol, ll = O.attend(q, k, v, pll, nl)
+    assert_outputs_close(g["o"], ol, g["lse"], ll)
+    say("[exact] theta=NaN (tau stop)")
+    g = run_gpu(q, k, v, S, 0.05, max_theta=float("nan"))
+    n_tau, traces = O.stop_points(q, k, pl, 0.05)
+    assert not stop_mismatches(g["n_I"], n_tau, traces, 0.05)
+
+
 def test_deterministic():
     spec = _spec(1, 4, 1, 2048, 32)
     q, k, v = make_stripe_inputs(spec)

@@ -14,6 +14,13 @@ SRC = pathlib.Path(S2O.__file__).read_text()
 
 # (name, exact text in oracle/s2o.py, replacement)
 MUTANTS = [
+    ("exact_mean_not_max", "mx = z.reshape(BLOCK, -1, BLOCK).max(axis=(0, 2))",
+     "mx = z.reshape(BLOCK, -1, BLOCK).mean(axis=(0, 2))"),
+    ("exact_strict", "sel = mx >= theta", "sel = mx > theta"),
+    ("exact_no_kappa", "z = kap * (q[rows] @ k[tiles.reshape(-1)].T)        # 64 x (t S)",
+     "z = (q[rows] @ k[tiles.reshape(-1)].T)"),
+    ("attend_mask_ignored", "far = tiles[np.asarray(tile_mask[(b, h, I)], bool)].reshape(-1)",
+     "far = tiles.reshape(-1)"),
     ("budget_off_by_one", "n_I[b, h, I] = min(budget, t * S // BLOCK)",
      "n_I[b, h, I] = min(budget + 1, t * S // BLOCK)"),
     ("budget_ignores_segment", "n_I[b, h, I] = min(budget, t * S // BLOCK)",

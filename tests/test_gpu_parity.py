@@ -273,3 +273,70 @@ def test_parity_llama_layer_n32k_full_plan_sampled_outputs():
     o_ref, lse_ref = O.attend(q, k, v, pl, n_use, blocks=blocks)
     err, mse = assert_outputs_close(g["o"], o_ref, g["lse"], lse_ref)
     say(f"   sampled blocks: max_abs={err:.3g} mse={mse:.3g}")
+
+
+def _sampled_check(q, k, v, S, tau, flags, pl, label, n_blocks=24, seed=11):
+    """One GPU run at full size against the oracle: every index array
+    bit-exact, then stop points and outputs of sampled query blocks (plus
+    the first and last block of the last head)."""
+    g = run_gpu(q, k, v, S, tau, flags)
+    assert_plan_equal(g, pl)
+    B, Hq, N = q.shape[:3]
+    nb = N // 64
+    rng = np.random.default_rng(seed)
+    blocks = [(int(b), int(h), int(I)) for b, h, I in zip(
+        rng.integers(0, B, n_blocks), rng.integers(0, Hq, n_blocks),
+        rng.integers(0, nb, n_blocks))]
+    blocks += [(B - 1, Hq - 1, nb - 1), (0, 0, 0)]
+    n_orc, traces = O.stop_points(q, k, pl, tau, blocks=blocks)
+    mask = n_orc >= 0
+    gn = np.where(mask, g["n_I"], -1)
+    ties = stop_mismatches(gn, n_orc, traces, tau)
+    n_use = n_orc.copy()
+    for b, h, I in ties:
+        n_use[b, h, I] = g["n_I"][b, h, I]
+    o_ref, lse_ref = O.attend(q, k, v, pl, n_use, blocks=blocks)
+    err, mse = assert_outputs_close(g["o"], o_ref, g["lse"], lse_ref)
+    say(f"   {label}: ties={len(ties)} mean_n_I={g['n_I'].mean():.2f} "
+        f"sampled max_abs={err:.3g} mse={mse:.3g}")
+    return g
+
+
+@pytest.mark.parametrize("cid", [3, 4, 5])
+def test_parity_full_size_sampled(cid):
+    """The 128K Llama-shaped layer (every tau of its sweep), the 128K
+    Qwen-shaped layer (every segment length) and the batch-4 64K layer
+    (S2O, KV permutation only, tau = 0 against dense attention) at their
+    full sizes in the launch configuration the benchmark times: index arrays
+    bit-exact, stop points and outputs of sampled blocks."""
+    cfg = get_config(cid)
+    say(f"[full] workload {cfg.name}: inputs")
+    q, k, v = make_stripe_inputs(cfg.spec)
+    runs = []
+    if cid == 3:
+        runs = [(cfg.segment, t_, 0) for t_ in cfg.taus]
+    elif cid == 4:
+        runs = [(S_, cfg.tau, 0) for S_ in cfg.segments]
+    else:
+        runs = [(cfg.segment, cfg.tau, 0),
+                (cfg.segment, cfg.tau, O.SA_NO_QPERM)]
+    plans = {}
+    for S, tau, flags in runs:
+        key = (S, flags)
+        if key not in plans:
+            say(f"[full] oracle plan S={S} flags={flags}")
+            plans[key] = O.plan(q, k, S, flags=flags)
+        say(f"[full] GPU S={S} tau={tau} flags={flags}")
+        _sampled_check(q, k, v, S, tau, flags, plans[key],
+                       f"S={S} tau={tau} flags={flags}")
+    if cid == 5:
+        say("[full] tau = 0 against dense attention on sampled rows")
+        g = run_gpu(q, k, v, cfg.segment, 0.0)
+        rng = np.random.default_rng(3)
+        N = q.shape[2]
+        rows = rng.integers(0, N, 12)
+        for b, h in [(0, 0), (3, 31), (2, 17)]:
+            od, ld = O.dense_causal(q, k, v, rows=rows, heads=[(b, h)])
+            err = np.abs(g["o"][b, h, rows] - od[b, h, rows]).max()
+            assert err <= 2e-2, err
+            assert np.abs(g["lse"][b, h, rows] - ld[b, h, rows]).max() <= 2e-3

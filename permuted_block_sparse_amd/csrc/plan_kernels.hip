@@ -47,18 +47,33 @@ __global__ __launch_bounds__(256) void k_pool_q(const uint16_t* __restrict__ q,
   }
 }
 
-// pooled[b, g, :] = sum over the G heads of group g and all chunks.
-__global__ __launch_bounds__(128) void k_pool_reduce(
+// pooled[b, g, :] = sum over the G heads of group g and all chunks: one
+// workgroup per (b, g), 8 slices of the G * nchunk partials per dimension,
+// 8 independent loads in flight per thread, then a sum over the slices
+// (integer: the order does not matter).
+__global__ __launch_bounds__(1024) void k_pool_reduce(
     const int64_t* __restrict__ part, int64_t* __restrict__ pooled, int Hq,
     int Hkv, int nchunk) {
+  __shared__ int64_t red[8][kHeadDim];
   const int bg = blockIdx.x, b = bg / Hkv, g = bg % Hkv, G = Hq / Hkv;
-  const int d = threadIdx.x;
-  int64_t s = 0;
-  for (int h = g * G; h < (g + 1) * G; ++h) {
-    const int64_t* p = part + ((size_t)(b * Hq + h) * nchunk) * kHeadDim + d;
-    for (int ch = 0; ch < nchunk; ++ch) s += p[(size_t)ch * kHeadDim];
+  const int d = threadIdx.x & (kHeadDim - 1), slice = threadIdx.x >> 7;
+  const int n = G * nchunk;  // partials of the group, in (head, chunk) order
+  const int64_t* p = part + ((size_t)(b * Hq + g * G) * nchunk) * kHeadDim + d;
+  int64_t a[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  int i = slice;
+  for (; i + 56 < n; i += 64) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) a[j] += p[(size_t)(i + 8 * j) * kHeadDim];
   }
-  pooled[(size_t)bg * kHeadDim + d] = s;
+  for (; i < n; i += 8) a[0] += p[(size_t)i * kHeadDim];
+  red[slice][d] = ((a[0] + a[1]) + (a[2] + a[3])) + ((a[4] + a[5]) + (a[6] + a[7]));
+  __syncthreads();
+  if (slice == 0) {
+    int64_t s = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) s += red[j][d];
+    pooled[(size_t)bg * kHeadDim + d] = s;
+  }
 }
 
 // --------------------------------------------------------------------------
@@ -464,8 +479,8 @@ hipError_t launch_pool_q(const PlanDims& d, const uint16_t* q, int64_t* part,
 
 hipError_t launch_pool_reduce(const PlanDims& d, const int64_t* part,
                               int64_t* pooled, hipStream_t s) {
-  hipLaunchKernelGGL(k_pool_reduce, dim3(d.B * d.Hkv), dim3(kHeadDim), 0, s,
-                     part, pooled, d.Hq, d.Hkv, d.n_pool_chunks);
+  hipLaunchKernelGGL(k_pool_reduce, dim3(d.B * d.Hkv), dim3(8 * kHeadDim), 0,
+                     s, part, pooled, d.Hq, d.Hkv, d.n_pool_chunks);
   return hipGetLastError();
 }
 

@@ -547,6 +547,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_fwd(AttnArgs a) {
   if (lane == 0 && half == 0) a.n_out[bh * (a.N / kBlock) + I] = n_visit;
 }
 
+int attention_blocks_per_wg() { return 4; }
+
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
   const int total = a.n_groups * a.wg_per_group;
   hipLaunchKernelGGL(k_attn_fwd, dim3(total), dim3(kThreads), 0, s, a);

@@ -82,5 +82,7 @@ struct AttnArgs {
   float exact_thr; // that test's threshold on the raw dot products (theta / kappa)
 };
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
+// Query blocks one attention workgroup processes (sets wg_per_group).
+int attention_blocks_per_wg();
 
 }  // namespace sa

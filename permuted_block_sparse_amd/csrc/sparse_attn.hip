@@ -262,7 +262,8 @@ int sparse_attn_prefill(const sa_plan* plan, const void* q, const void* k,
   a.T = d.T;
   a.G = d.G;
   const int qblocks = d.G * (d.S / kBlock);
-  a.wg_per_group = (qblocks + 3) / 4;
+  const int bpw = attention_blocks_per_wg();
+  a.wg_per_group = (qblocks + bpw - 1) / bpw;
   a.n_groups = d.B * d.Hkv * d.T;
   // a fixed budget or the exact max test replaces the stop test (tau = 0:
   // no estimate stops); the exact test takes precedence over a budget

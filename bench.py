@@ -71,9 +71,9 @@ def source_hash(path):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on exactly one GPU: this build has no multi-GPU "
-              "path (the method shards over independent KV heads with no "
-              "communication; see DESIGN.md). Use --gpus 1.", file=sys.stderr)
+        print("bench.py runs on exactly one GPU: there is no multi-GPU path "
+              "(the method would shard over independent KV heads with no "
+              "communication between GPUs). Use --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -15,10 +15,12 @@
  * Two calls make up the path:
  *   sparse_attn_plan     -- the importance estimator and the index builder
  *                           (both orders and the causally restricted key
- *                           lists), integer-exact;
- *   sparse_attn_prefill  -- the gather attention kernel with the tau stop
- *                           and the scatter of each output row back to its
- *                           original position.
+ *                           lists, integer-exact) and the stop points of
+ *                           the tau stop, scanned from pooled means;
+ *   sparse_attn_prefill  -- the gather attention kernel, which stops each
+ *                           query block at its stop point, and the scatter
+ *                           of each output row back to its original
+ *                           position.
  *
  * Conventions for every entry point:
  *   - Tensors are caller-owned DEVICE pointers, bfloat16 (raw 16-bit
@@ -122,8 +124,15 @@ size_t sparse_attn_workspace_bytes(const sa_params* p);
  *   5. contrast vectors C_t = t S * sum_{j in L_t[0:64]} fx(k_j)
  *                            - 64 * sum_{j < t S} fx(k_j);
  *   6. query scores u_i = fx(q_i) . C_seg(i) (0 in segment 0);
- *   7. segment-local query order pi_Q: u descending, ties by index.
- * All scores are exact integers, so the orders are reproducible bit for bit.
+ *   7. segment-local query order pi_Q: u descending, ties by index;
+ *   8. the stop point n_I of every query block for the plan's tau (the rule
+ *      is stated at sparse_attn_prefill): every estimate there is a mean
+ *      logit, equal to (sum of the block's 64 queries) . (sum of the 64
+ *      keys) / 4096, so n_I follows from fp32 sums of the blocks' queries
+ *      and of the keys of the local blocks and of the tiles of L_t, with
+ *      the running total and the test in float64.
+ * All scores of steps 1-7 are exact integers, so the orders are
+ * reproducible bit for bit.
  * q, k: device pointers (see conventions); workspace: device buffer of at
  * least sparse_attn_workspace_bytes(p) bytes, 256-byte aligned. On success
  * *out receives a new plan (free with sparse_attn_plan_destroy).
@@ -135,7 +144,7 @@ int sparse_attn_plan(const sa_params* p, const void* q, const void* k,
 /*
  * The attention (S2O page, Summary: fetch the indexed tokens into on-chip
  * memory, process blocks from most to least important, stop once a block's
- * score falls under tau). One launch. For each 64-row query block I (rows
+ * score falls under tau). For each 64-row query block I (rows
  * pi_Q[64 I .. 64 I + 63], all in segment t):
  *   - the dense local window: exact causal attention against the keys of
  *     segment t, and its estimated mass
@@ -149,7 +158,10 @@ int sparse_attn_plan(const sa_params* p, const void* q, const void* k,
  * from (not checked). o: device [batch, heads_q, seq_len, 128] bfloat16,
  * fully overwritten. lse (may be NULL): device [batch, heads_q, seq_len]
  * float32, natural-log log-sum-exp of kappa q.k over each row's key set.
- * The stop points n_I are recorded in the workspace (see export).
+ * The stop points come from the plan (export N_I). After a setter below or
+ * sparse_attn_plan_set_kv_order changed what they depend on, this call
+ * first rescans them on `stream` (one extra launch), then launches the
+ * attention. A plan must not be used by two calls at once.
  */
 int sparse_attn_prefill(const sa_plan* plan, const void* q, const void* k,
                         const void* v, void* o, float* lse,
@@ -193,7 +205,9 @@ size_t sparse_attn_plan_export_bytes(const sa_plan* plan, int what);
 
 /* Copy one plan array to host memory `host_dst` (at least
  * sparse_attn_plan_export_bytes bytes) after the work enqueued on `stream`
- * so far; synchronizes `stream`. N_I is meaningful after a prefill. */
+ * so far; synchronizes `stream`. N_I holds the stop points after
+ * sparse_attn_plan (and after every prefill), and after a prefill with the
+ * exact maximum test the number of tiles each block attended. */
 int sparse_attn_plan_export(const sa_plan* plan, int what, void* host_dst,
                             size_t bytes, hipStream_t stream);
 

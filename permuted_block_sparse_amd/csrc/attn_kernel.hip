@@ -1,34 +1,37 @@
 // Gather attention with the early stop (S2O page, Summary): the kernel
 // fetches the indexed tokens into on-chip memory (LDS), processes key/value
 // blocks from most to least important with an online softmax (FlashAttention
-// tiling) and stops a query block once the next block's estimated share of
-// the attention mass falls below tau. Outputs go back to their original rows
-// (no tensor is moved).
+// tiling) and stops each query block at its stop point n_I, the first tile
+// whose estimated share of the attention mass falls below tau. The stop
+// points depend only on pooled means and are scanned before this launch;
+// the loop itself carries no decision. Outputs go back to their original
+// rows (no tensor is moved).
 //
 // Work decomposition (gfx950, wave64, 2 waves per SIMD): one workgroup = 8
 // waves = 4 query blocks of 64 rows that share the same KV head g and
 // segment t, hence the same key tiles (dense local window = segment t's
 // keys; sparse tiles = L_t). Wave w holds rows 32 (w / 4) .. + 31 of query
 // block w % 4; both halves of a block sit on the same SIMD. K and V tiles
-// are gathered into LDS once per workgroup and read by all 8 waves. The two
-// halves of a block hand each other their partial tile sums through an LDS
-// mailbox (a pairwise handshake, no workgroup barrier), so both take the
-// same stop decision from the same bits.
+// are gathered into LDS once per workgroup and read by all 8 waves; the
+// workgroup runs to the largest stop point of its blocks, and a wave whose
+// block has stopped only helps with the gathers.
 //
 // Pipeline: the local blocks and then the sparse tiles form one sequence of
 // steps. LDS holds two K/V tile buffers. Step s computes S of tile s from
-// buffer s % 2 and posts its partial tile sum; while the other half of the
-// block finishes its own, every lane stores its share of tile s + 1's rows
+// buffer s % 2; then every lane stores its share of tile s + 1's rows
 // (loaded into registers during step s - 1) into the other buffer and
 // issues the global loads of tile s + 2's rows and step s + 3's indices;
-// then the stop decision and the softmax / PV of tile s. One barrier per
-// step. The rows have a whole step to arrive, and the LDS stores overlap
-// the half-pair handshake instead of the MFMA phases.
+// then the softmax / PV of tile s. One barrier per step; the rows have a
+// whole step to arrive.
+//
+// Exact per-block max mode (the BSFA page's test, instead of the stop): every
+// tile of L_t is scored and attended iff the largest logit of the 64 x 64
+// tile reaches the threshold; the two halves of a block hand each other
+// their tile maxima through an LDS mailbox so both decide on the same bits.
 //
 // Per wave and 64-key tile:
 //   S^T = K Q^T   : 2 v_mfma_f32_32x32x16_bf16 blocks over d = 128, Q^T
 //                   operands held in registers for the whole run;
-//   mean of S     : the mean-pooled logit of the 64 x 64 tile (both halves);
 //   online softmax: one query row per lane pair (lane, lane ^ 32), fp32,
 //                   exp2 domain; the running max is raised only when a row's
 //                   max exceeds it by more than 2^8 (exact: o = acc / l for
@@ -94,33 +97,8 @@ __device__ __forceinline__ float sum_xor32(float x) {
                                             __float_as_uint(x), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
-__device__ __forceinline__ float sum_xor16(float x) {
-  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x),
-                                            __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-__device__ __forceinline__ int isum_xor16(int x) {
-  auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
-  return (int)r[0] + (int)r[1];
-}
-__device__ __forceinline__ int isum_xor32(int x) {
-  auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
-  return (int)r[0] + (int)r[1];
-}
 
-// Wave-wide sums; every step adds two equal-by-symmetry partial sums, so all
-// lanes end with the same bits (read from lane 0 to make it uniform).
-__device__ __forceinline__ float wave_sum(float x) {
-  x += __int_as_float(dpp_xor1(__float_as_int(x)));
-  x += __int_as_float(dpp_xor2(__float_as_int(x)));
-  x += __int_as_float(dpp_half_mirror(__float_as_int(x)));
-  x += __int_as_float(dpp_mirror(__float_as_int(x)));
-  x = sum_xor16(x);
-  x = sum_xor32(x);
-  return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(
-                                       __builtin_bit_cast(int, x)));
-}
-
+// Wave-wide maximum, made uniform through lane 0.
 __device__ __forceinline__ float wave_max(float x) {
   x = fmaxf(x, __int_as_float(dpp_xor1(__float_as_int(x))));
   x = fmaxf(x, __int_as_float(dpp_xor2(__float_as_int(x))));
@@ -132,16 +110,6 @@ __device__ __forceinline__ float wave_max(float x) {
   x = max_xor32(x);
   return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(
                                        __builtin_bit_cast(int, x)));
-}
-
-__device__ __forceinline__ int wave_sum_int(int x) {
-  x += dpp_xor1(x);
-  x += dpp_xor2(x);
-  x += dpp_half_mirror(x);
-  x += dpp_mirror(x);
-  x = isum_xor16(x);
-  x = isum_xor32(x);
-  return __builtin_amdgcn_readfirstlane(x);
 }
 
 __device__ __forceinline__ int wave_max_int(int x) {
@@ -262,14 +230,6 @@ __device__ __forceinline__ float lane_max(const f32x16 (&sacc)[2]) {
   return fmaxf(fmaxf(v4[0], v4[1]), fmaxf(v4[2], v4[3]));
 }
 
-__device__ __forceinline__ float lane_sum(const f32x16 (&sacc)[2]) {
-  const f32x16 t = sacc[0] + sacc[1];
-  float s4[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r)
-    s4[r] = (t[r] + t[r + 8]) + (t[r + 4] + t[r + 12]);
-  return (s4[0] + s4[2]) + (s4[1] + s4[3]);
-}
 
 // Online softmax update of this lane's query row, then O^T += V^T P^T.
 // m is kept in the exp2 domain (m = reference logit * c2).
@@ -327,12 +287,17 @@ __device__ __forceinline__ void softmax_pv(const char* Vt, f32x16 (&sacc)[2],
 __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 constexpr int kSpinLimit = 1 << 22;
 
+// kExact = false: each block attends its dense local window and the first
+// n_I tiles of L_t, n_I given (the early stop's stop points). kExact = true:
+// the exact per-block max test decides every tile of L_t in the loop.
+template <bool kExact>
 __global__ __launch_bounds__(kThreads, 1) void k_attn_fwd(AttnArgs a) {
   // two K/V tile buffers of 2 x 16 KB
   __shared__ __attribute__((aligned(1024))) char tiles[2][2 * kTileBytes];
   __shared__ int wave_maxrow[kWaves];
-  __shared__ int busy[2][kWaves];  // per step parity: wave still attending
-  // per-wave mailbox: (step + 1) << 32 | bits of the wave's partial sum
+  __shared__ int wave_ntiles[kWaves];
+  // exact mode: per-wave mailbox, (step + 1) << 32 | bits of the wave's
+  // tile maximum
   __shared__ unsigned long long mailbox[kWaves];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int lq = lane & 31, lh = lane >> 5;
@@ -363,8 +328,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_fwd(AttnArgs a) {
 
   const size_t bh = (size_t)b * a.Hq + h;
   const int32_t* pq = a.pi_q + bh * a.N + (size_t)I * kBlock;
-  const int iq = min(max(pq[32 * half + lq], 0), a.N - 1);         // my row
-  const int iq_o = min(max(pq[32 * (1 - half) + lq], 0), a.N - 1);  // other
+  const int iq = min(max(pq[32 * half + lq], 0), a.N - 1);  // my row
   const uint16_t* qh = a.q + bh * a.N * kHeadDim;
   const uint16_t* kbase = a.k + (size_t)bg * a.N * kHeadDim;
   const uint16_t* vbase = a.v + (size_t)bg * a.N * kHeadDim;
@@ -381,23 +345,27 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_fwd(AttnArgs a) {
   for (int db = 0; db < 4; ++db) oacc[db] = f32x16{};
   float m = -INFINITY, l = 0.f;
   f32x16 sacc[2];
-  double acc = 0.0;  // running estimated mass (dense window + visited tiles)
 
-  // ---- the step sequence: ndiag local blocks, then the tiles of L_t.
+  // ---- the step sequence: ndiag local blocks, then the tiles of L_t up to
+  // the largest stop point of the workgroup's blocks.
   const int seg0 = t * a.S;
+  const int ntl = t * bps;  // tiles of L_t
+  int32_t* nI_ptr = a.n_I + bh * (a.N / kBlock) + I;
+  const int nI = !valid ? 0 : kExact ? ntl : min(max(*nI_ptr, 0), ntl);
   const int myrow = wave_max_int(iq);
   if (lane == 0) {
     wave_maxrow[wave] = valid ? myrow : -1;
-    mailbox[wave] = 0ull;
+    wave_ntiles[wave] = nI;
+    if (kExact) mailbox[wave] = 0ull;
   }
   __syncthreads();
-  int wgmax = -1;
+  int wgmax = -1, ntiles = 0;
 #pragma unroll
-  for (int w = 0; w < kWaves; ++w) wgmax = max(wgmax, wave_maxrow[w]);
+  for (int w = 0; w < kWaves; ++w) {
+    wgmax = max(wgmax, wave_maxrow[w]);
+    ntiles = max(ntiles, wave_ntiles[w]);
+  }
   const int ndiag = min(max((wgmax - seg0) / kBlock + 1, 1), bps);
-  const int ntiles = a.local_only ? 0
-                     : a.budget >= 0 ? min(t * bps, a.budget)
-                                     : t * bps;
   const int nsteps = ndiag + ntiles;
   const int32_t* Lt =
       a.L + (size_t)bg * a.list_len + (size_t)a.S * t * (t - 1) / 2;
@@ -430,66 +398,42 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_fwd(AttnArgs a) {
   int raw = *key_src(2, rg);
   __syncthreads();
 
-  bool active = valid;
-  // exact per-block max mode: n_I counts the attended tiles
-  int n_visit = a.exact ? 0 : (t > 0 ? ntiles : 0);
+  int n_visit = 0;  // exact mode: tiles attended
   for (int s = 0; s < nsteps; ++s) {
     const char* Kt = tiles[s & 1];
     const char* Vt = Kt + kTileBytes;
 
-    // local block (s < ndiag): exact causal attention, mass estimate from
-    // the mean logit of the whole 64 x 64 block weighted by its visible
-    // pairs; sparse tile: estimate, stop test, then attention.
+    // local block (s < ndiag): exact causal attention of the rows that see
+    // any of its keys; sparse tile: attention up to the stop point (exact
+    // mode: the max test first)
     const bool local = s < ndiag;
     const int j0 = seg0 + s * kBlock;
-    int nvis = 0;
-    if (local) {
-      const int nv_lane = lh == 0 ? min(max(iq - j0 + 1, 0), kBlock) +
-                                        min(max(iq_o - j0 + 1, 0), kBlock)
-                                  : 0;
-      nvis = wave_sum_int(nv_lane);
-    }
-    // the halves of a block always agree on `compute`
-    const bool compute = local ? (valid && nvis > 0) : active;
+    const bool compute = valid && (local ? myrow >= j0 : (s - ndiag) < nI);
     typedef __attribute__((address_space(3))) volatile unsigned long long
         lds_u64;
     lds_u64* box = (lds_u64*)mailbox;
     float ps = 0.f;
     if (compute) {
       qk_tile(Kt, qr, sacc, ra);
-      // the half's share of the tile statistic: its partial tile sum (mean
-      // estimate), or its tile maximum (exact per-block max mode)
-      ps = a.exact ? wave_max(lane_max(sacc)) : wave_sum(lane_sum(sacc));
-      if (lane == 0)
-        box[wave] = ((unsigned long long)(s + 1) << 32) | __float_as_uint(ps);
+      if (kExact && !local) {
+        // the half's tile maximum, for the other half of the block
+        ps = wave_max(lane_max(sacc));
+        if (lane == 0)
+          box[wave] = ((unsigned long long)(s + 1) << 32) | __float_as_uint(ps);
+      }
     }
-    // while the other half finishes its partial sum: step s + 1's rows
-    // (loaded during step s - 1) -> the other buffer, which held step
-    // s - 1's tile (read by every wave before the last barrier); then the
-    // loads of step s + 2's rows and of step s + 3's indices
+    // step s + 1's rows (loaded during step s - 1) -> the other buffer,
+    // which held step s - 1's tile (read by every wave before the last
+    // barrier); then the loads of step s + 2's rows and of step s + 3's
+    // indices
     if (s + 1 < nsteps)
       store_rows(tiles[(s + 1) & 1], tiles[(s + 1) & 1] + kTileBytes, nxt,
                  sta);
     if (s + 2 < nsteps) nxt = stage(s + 2, raw);
     raw = *key_src(s + 3, rg);
     if (compute) {
-      // wait for the other half's partial sum of this step (bounded)
-      unsigned long long other;
-      int spins = 0;
-      while (true) {
-        other = box[wave ^ 4];
-        if ((other >> 32) == (unsigned long long)(s + 1) ||
-            ++spins >= kSpinLimit)
-          break;
-        __builtin_amdgcn_s_sleep(1);
-      }
-      const float po = __uint_as_float((uint32_t)other);
-      const float ssum = half == 0 ? ps + po : po + ps;  // same order for both
-      const float ex = __builtin_amdgcn_exp2f(
-          ssum * (float)(a.kappa * 1.4426950408889634 / (kBlock * kBlock)));
       bool take = true;
       if (local) {
-        acc += ((double)nvis / kBlock) * (double)ex;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -497,33 +441,26 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_fwd(AttnArgs a) {
             const int jk = j0 + kb * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
             if (jk > iq) sacc[kb][r] = -INFINITY;
           }
-      } else if (a.exact) {
-        // exact per-block max test: attend the tile iff its largest logit
-        // reaches the threshold (both halves take max of the same two
-        // values); no stop
+      } else if (kExact) {
+        // wait for the other half's maximum of this step (bounded); both
+        // halves take max of the same two values
+        unsigned long long other;
+        int spins = 0;
+        while (true) {
+          other = box[wave ^ 4];
+          if ((other >> 32) == (unsigned long long)(s + 1) ||
+              ++spins >= kSpinLimit)
+            break;
+          __builtin_amdgcn_s_sleep(1);
+        }
+        const float po = __uint_as_float((uint32_t)other);
         take = fmaxf(ps, po) >= a.exact_thr;
         n_visit += take ? 1 : 0;
-      } else {
-        // share est / (acc + est) < tau, without the division
-        const double est = kBlock * (double)ex;
-        if (est < a.tau * (acc + est)) {
-          active = false;
-          n_visit = s - ndiag;
-          take = false;
-        } else {
-          acc += est;
-        }
       }
       if (take) softmax_pv(Vt, sacc, oacc, m, l, a.c2, ra);
     }
-    // one barrier, which also combines the waves' `active` flags
-    if (lane == 0) busy[s & 1][wave] = active ? 1 : 0;
     wait_lgkm0();
     __builtin_amdgcn_s_barrier();
-    int any = 0;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) any |= busy[s & 1][w];
-    if (!any) break;
   }
   __builtin_amdgcn_s_waitcnt(0);  // index loads of steps never taken
 
@@ -544,14 +481,18 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_fwd(AttnArgs a) {
     }
   if (a.lse != nullptr && lh == 0)
     a.lse[bh * a.N + iq] = (m + log2f(l)) * ln2;
-  if (lane == 0 && half == 0) a.n_out[bh * (a.N / kBlock) + I] = n_visit;
+  if (kExact && lane == 0 && half == 0) *nI_ptr = n_visit;
 }
 
 int attention_blocks_per_wg() { return 4; }
 
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
   const int total = a.n_groups * a.wg_per_group;
-  hipLaunchKernelGGL(k_attn_fwd, dim3(total), dim3(kThreads), 0, s, a);
+  if (a.exact)
+    hipLaunchKernelGGL(k_attn_fwd<true>, dim3(total), dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL(k_attn_fwd<false>, dim3(total), dim3(kThreads), 0, s,
+                       a);
   return hipGetLastError();
 }
 

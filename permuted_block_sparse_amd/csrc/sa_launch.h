@@ -59,6 +59,25 @@ hipError_t launch_restrict(const PlanDims& d, const int32_t* pi_k,
                            int32_t* cnt, int32_t* cum, int32_t* L,
                            hipStream_t s);
 
+// ---- stop points (pooled means -> n_I)
+// Sum of the 64 query rows of every block of pi_Q: qsum, fp32
+// [B, Hq, N / 64, 128].
+hipError_t launch_block_qsum(const PlanDims& d, const uint16_t* q,
+                             const int32_t* pi_q, float* qsum, hipStream_t s);
+struct StopArgs {
+  const uint16_t* k;
+  const int32_t* L;
+  const int32_t* pi_q;
+  const float* qsum;
+  int32_t* n_I;     // out: [B, Hq, N / 64]
+  long long list_len;
+  int B, Hq, Hkv, N, S, T, G;
+  double tau;
+  float c2;         // kappa * log2(e)
+  int fixed;        // >= 0: n_I = min(fixed, t S / 64), no scan
+};
+hipError_t launch_stop_scan(const StopArgs& a, hipStream_t s);
+
 // ---- attention
 struct AttnArgs {
   const uint16_t* q;
@@ -68,17 +87,13 @@ struct AttnArgs {
   float* lse;
   const int32_t* pi_q;
   const int32_t* L;
-  int32_t* n_out;
+  int32_t* n_I;  // stop points: read; exact mode: tiles attended, written
   long long list_len;
   int B, Hq, Hkv, N, S, T, G;
   int wg_per_group;
   int n_groups;
-  double tau;
-  double kappa;
-  float c2;  // kappa * log2(e)
-  int local_only;  // 1: no tile of L_t is visited (dense local window only)
-  int budget;      // >= 0: at most this many tiles of L_t (tau is then 0)
-  int exact;       // 1: exact per-block max test instead of the tau stop
+  float c2;        // kappa * log2(e)
+  int exact;       // 1: exact per-block max test instead of the stop points
   float exact_thr; // that test's threshold on the raw dot products (theta / kappa)
 };
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s);

@@ -24,7 +24,7 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 struct Layout {
   size_t pool_part, pooled, vscore, blocksum, segsum, contrast, u;
   size_t key_a, idx_a, key_b, idx_b;
-  size_t pi_k, L, pi_q, n_I, rcnt, rcum;
+  size_t pi_k, L, pi_q, n_I, rcnt, rcum, qsum;
   size_t total;
 };
 
@@ -94,6 +94,7 @@ Layout layout_of(const PlanDims& d) {
   L.n_I = take(nbh * (d.N / kBlock) * sizeof(int32_t));
   L.rcnt = take(nbg * d.n_restrict_chunks * d.T * sizeof(int32_t));
   L.rcum = take(nbg * d.n_restrict_chunks * d.T * sizeof(int32_t));
+  L.qsum = take(nbh * (d.N / kBlock) * kHeadDim * sizeof(float));
   L.total = off;
   return L;
 }
@@ -104,6 +105,10 @@ struct sa_plan {
   sa_params p;
   int32_t budget = -1;  // >= 0: fixed tile budget instead of the tau stop
   double max_theta = std::numeric_limits<double>::quiet_NaN();  // exact test
+  // n_I holds the stop points of the current settings (set by the stop
+  // scan; cleared by every setter and by an exact-mode prefill, whose n_I
+  // counts attended tiles)
+  mutable bool stops_valid = false;
   PlanDims d;
   Layout lay;
   char* ws;
@@ -161,7 +166,51 @@ int build_from_kv_order(sa_plan* pl, hipStream_t s) {
         pl->at<uint64_t>(pl->lay.key_b), pl->at<int32_t>(pl->lay.idx_b),
         pl->at<int32_t>(pl->lay.pi_q), s);
   }
+  if (e != hipSuccess) return SA_ERR_HIP;
+  // the blocks' query sums, for the stop scan
+  e = launch_block_qsum(d, static_cast<const uint16_t*>(pl->q),
+                        pl->at<int32_t>(pl->lay.pi_q),
+                        pl->at<float>(pl->lay.qsum), s);
   return hip_status(e);
+}
+
+bool exact_mode(const sa_plan* pl) {
+  return !std::isnan(pl->max_theta) && !(pl->p.flags & SA_LOCAL_ONLY);
+}
+
+// n_I of the plan's current settings: the tau stop scanned from pooled
+// means, or a fixed count (dense local window only: 0; fixed budget K:
+// min(K, t S / 64); tau = 0 or SA_NO_EARLYSTOP: every tile of L_t).
+int run_stop_scan(const sa_plan* pl, hipStream_t s) {
+  const PlanDims& d = pl->d;
+  StopArgs a;
+  a.k = static_cast<const uint16_t*>(pl->k);
+  a.L = pl->at<int32_t>(pl->lay.L);
+  a.pi_q = pl->at<int32_t>(pl->lay.pi_q);
+  a.qsum = pl->at<float>(pl->lay.qsum);
+  a.n_I = pl->at<int32_t>(pl->lay.n_I);
+  a.list_len = (long long)d.list_len;
+  a.B = d.B;
+  a.Hq = d.Hq;
+  a.Hkv = d.Hkv;
+  a.N = d.N;
+  a.S = d.S;
+  a.T = d.T;
+  a.G = d.G;
+  a.tau = pl->p.tau;
+  a.c2 = (float)(1.4426950408889634074 / std::sqrt((double)kHeadDim));
+  if (pl->p.flags & SA_LOCAL_ONLY)
+    a.fixed = 0;
+  else if (pl->budget >= 0)
+    a.fixed = pl->budget;
+  else if ((pl->p.flags & SA_NO_EARLYSTOP) || pl->p.tau == 0.0)
+    a.fixed = std::numeric_limits<int>::max();
+  else
+    a.fixed = -1;
+  const hipError_t e = launch_stop_scan(a, s);
+  if (e != hipSuccess) return SA_ERR_HIP;
+  pl->stops_valid = true;
+  return SA_OK;
 }
 
 }  // namespace
@@ -229,6 +278,7 @@ int sparse_attn_plan(const sa_params* p, const void* q, const void* k,
   }
   int rc = hip_status(e);
   if (rc == SA_OK) rc = build_from_kv_order(pl, stream);
+  if (rc == SA_OK) rc = run_stop_scan(pl, stream);
   if (rc != SA_OK) {
     delete pl;
     return rc;
@@ -252,7 +302,7 @@ int sparse_attn_prefill(const sa_plan* plan, const void* q, const void* k,
   a.lse = lse;
   a.pi_q = plan->at<int32_t>(plan->lay.pi_q);
   a.L = plan->at<int32_t>(plan->lay.L);
-  a.n_out = plan->at<int32_t>(plan->lay.n_I);
+  a.n_I = plan->at<int32_t>(plan->lay.n_I);
   a.list_len = (long long)d.list_len;
   a.B = d.B;
   a.Hq = d.Hq;
@@ -265,31 +315,32 @@ int sparse_attn_prefill(const sa_plan* plan, const void* q, const void* k,
   const int bpw = attention_blocks_per_wg();
   a.wg_per_group = (qblocks + bpw - 1) / bpw;
   a.n_groups = d.B * d.Hkv * d.T;
-  // a fixed budget or the exact max test replaces the stop test (tau = 0:
-  // no estimate stops); the exact test takes precedence over a budget
-  a.exact = std::isnan(plan->max_theta) ? 0 : 1;
-  a.tau = (plan->p.flags & SA_NO_EARLYSTOP) || plan->budget >= 0 || a.exact
-              ? 0.0
-              : plan->p.tau;
-  a.local_only = (plan->p.flags & SA_LOCAL_ONLY) ? 1 : 0;
-  a.budget = a.exact ? -1 : plan->budget;
+  // the exact max test takes precedence over a budget and over tau; the
+  // dense local window only takes precedence over everything
+  a.exact = exact_mode(plan) ? 1 : 0;
   a.exact_thr = a.exact ? (float)(plan->max_theta *
                                   std::sqrt((double)kHeadDim))
                         : 0.f;
-  a.kappa = 1.0 / std::sqrt((double)kHeadDim);
-  a.c2 = (float)(a.kappa * 1.4426950408889634074);
+  a.c2 = (float)(1.4426950408889634074 / std::sqrt((double)kHeadDim));
+  if (!a.exact && !plan->stops_valid) {
+    const int rc = run_stop_scan(plan, stream);
+    if (rc != SA_OK) return rc;
+  }
+  if (a.exact) plan->stops_valid = false;
   return hip_status(launch_attention(a, stream));
 }
 
 int sparse_attn_plan_set_max_threshold(sa_plan* plan, double theta) {
   if (plan == nullptr) return SA_ERR_NULL_POINTER;
   plan->max_theta = theta;
+  plan->stops_valid = false;
   return SA_OK;
 }
 
 int sparse_attn_plan_set_budget(sa_plan* plan, int32_t tiles) {
   if (plan == nullptr) return SA_ERR_NULL_POINTER;
   plan->budget = tiles < 0 ? -1 : tiles;
+  plan->stops_valid = false;
   return SA_OK;
 }
 
@@ -297,6 +348,7 @@ int sparse_attn_plan_set_tau(sa_plan* plan, double tau) {
   if (plan == nullptr) return SA_ERR_NULL_POINTER;
   if (!(tau >= 0.0) || std::isinf(tau)) return SA_ERR_INVALID_ARG;
   plan->p.tau = tau;
+  plan->stops_valid = false;
   return SA_OK;
 }
 
@@ -351,7 +403,9 @@ int sparse_attn_plan_set_kv_order(sa_plan* plan, const void* pi_k,
   hipError_t e = hipMemcpyAsync(plan->ws + plan->lay.pi_k, pi_k, bytes,
                                 hipMemcpyDeviceToDevice, stream);
   if (e != hipSuccess) return SA_ERR_HIP;
-  return build_from_kv_order(plan, stream);
+  plan->stops_valid = false;
+  const int rc = build_from_kv_order(plan, stream);
+  return rc != SA_OK ? rc : run_stop_scan(plan, stream);
 }
 
 void sparse_attn_plan_destroy(sa_plan* plan) { delete plan; }

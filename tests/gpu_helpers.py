@@ -13,8 +13,9 @@ MAX_ABS_TOL = 2e-2
 MSE_TOL = 1e-4
 LSE_TOL = 2e-3
 # A stop decision is a near-tau tie when the oracle's ratio is within this
-# relative distance of tau: the GPU evaluates the tile's mean logit in fp32
-# from MFMA products, the oracle in float64.
+# relative distance of tau: the GPU evaluates a tile's mean logit in fp32
+# (sum of the block's queries . sum of the tile's keys), the oracle in
+# float64.
 TIE_REL = 1e-4
 
 

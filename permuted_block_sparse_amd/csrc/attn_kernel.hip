@@ -426,10 +426,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_fwd(AttnArgs a) {
     // which held step s - 1's tile (read by every wave before the last
     // barrier); then the loads of step s + 2's rows and of step s + 3's
     // indices
-    if (s + 1 < nsteps)
-      store_rows(tiles[(s + 1) & 1], tiles[(s + 1) & 1] + kTileBytes, nxt,
-                 sta);
-    if (s + 2 < nsteps) nxt = stage(s + 2, raw);
+    store_rows(tiles[(s + 1) & 1], tiles[(s + 1) & 1] + kTileBytes, nxt,
+               sta);
+    nxt = stage(s + 2, raw);
     raw = *key_src(s + 3, rg);
     if (compute) {
       bool take = true;

@@ -17,17 +17,22 @@
 // block has stopped only helps with the gathers.
 //
 // Pipeline: the local blocks and then the sparse tiles form one sequence of
-// steps. LDS holds two K/V tile buffers. Step s computes S of tile s from
-// buffer s % 2; then every lane stores its share of tile s + 1's rows
-// (loaded into registers during step s - 1) into the other buffer and
-// issues the global loads of tile s + 2's rows and step s + 3's indices;
-// then the softmax / PV of tile s. One barrier per step; the rows have a
-// whole step to arrive.
+// steps, and each wave overlaps its matrix and vector work within a step.
+// LDS holds three K/V tile buffers and each wave two sets of logit
+// registers. Step s: row maximum (and the rare rescale) of tile s's
+// logits; the QK MFMAs of tile s + 1 interleaved with the exponentials of
+// tile s; the PV MFMAs of tile s; tile s + 2's rows (loaded into registers
+// during step s - 1) into the buffer that held tile s - 1; the loads of
+// tile s + 3's rows and of step s + 4's indices. One barrier per step. A
+// wave whose block has stopped (or that holds no rows) runs the same
+// instructions as a no-op, so no branch splits the MFMA and VALU work.
 //
 // Exact per-block max mode (the BSFA page's test, instead of the stop): every
 // tile of L_t is scored and attended iff the largest logit of the 64 x 64
 // tile reaches the threshold; the two halves of a block hand each other
 // their tile maxima through an LDS mailbox so both decide on the same bits.
+// This mode keeps the plain order per step (QK, row stores and loads,
+// handshake, softmax / PV) over two of the buffers.
 //
 // Per wave and 64-key tile:
 //   S^T = K Q^T   : 2 v_mfma_f32_32x32x16_bf16 blocks over d = 128, Q^T
@@ -283,6 +288,92 @@ __device__ __forceinline__ void softmax_pv(const char* Vt, f32x16 (&sacc)[2],
   }
 }
 
+// The online softmax of one tile in pieces (row max and rescale here, the
+// exponentials in qk_exp, the PV product in pv_tile), so that the QK MFMAs
+// of the next tile can be interleaved with the exponentials of this one.
+// `active` false turns the step into a no-op with the same instructions:
+// no rescale, every p = 0 (the reference is +inf), nothing added.
+// Returns the reference the exponentials subtract.
+__device__ __forceinline__ float row_rescale(const f32x16 (&sacc)[2],
+                                             f32x16 (&oacc)[4], float& m,
+                                             float& l, float c2, bool active) {
+  float v = -INFINITY;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) v = fmaxf(v, sacc[kb][r]);
+  const float mx = max_xor32(v) * c2 + (active ? 0.f : -INFINITY);
+  if (__builtin_amdgcn_ballot_w64(mx > m + kRescaleSlack) != 0) {
+    const float mnew = fmaxf(m, mx);
+    const float alpha = m == mnew ? 1.f : __builtin_amdgcn_exp2f(m - mnew);
+    l *= alpha;
+#pragma unroll
+    for (int db = 0; db < 4; ++db) oacc[db] *= alpha;
+    m = mnew;
+  }
+  return !active ? INFINITY : m == -INFINITY ? 0.f : m;
+}
+
+__device__ __forceinline__ void pv_tile(const char* Vt, const f32x16 (&sacc)[2],
+                                        f32x16 (&oacc)[4], const ReadAddr& ra) {
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const int kb = s >> 1, half = s & 1;
+    bf16x8 pb;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) pb[e] = (__bf16)sacc[kb][8 * half + e];
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      const int id = ((2 * kb + half) * 4 + db) * 2;
+      const char* p = Vt + id * 512 + ra.vofs[db & 1];
+      const s16x4 lo = lds_read_tr16(p);
+      const s16x4 hi = lds_read_tr16(p + 512);
+      const s16x8 cat = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      oacc[db] = mfma32(__builtin_bit_cast(bf16x8, cat), pb, oacc[db]);
+    }
+  }
+}
+
+// The QK of the next tile (into nxs) interleaved with the exponentials of
+// this one (cur, in place): per k-step 2 MFMAs and 4 exponentials, the K
+// operands one k-step ahead. Returns the row sum of the new p.
+__device__ __forceinline__ float qk_exp(const char* Kt, const bf16x8 (&qr)[8],
+                                        f32x16 (&nxs)[2], f32x16 (&cur)[2],
+                                        float c2, float muse,
+                                        const ReadAddr& ra) {
+  nxs[0] = f32x16{};
+  nxs[1] = f32x16{};
+  bf16x8 op[2][2];
+  auto load = [&](int s, bf16x8 (&o)[2]) {
+    const char* p = Kt + s * 1024 + ra.kofs[s & 3];
+    o[0] = *reinterpret_cast<const bf16x8*>(p);
+    o[1] = *reinterpret_cast<const bf16x8*>(p + 8 * 1024);
+  };
+  float rs = 0.f;
+  load(0, op[0]);
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    if (s + 1 < 8) load(s + 1, op[(s + 1) & 1]);
+    nxs[0] = mfma32(op[s & 1][0], qr[s], nxs[0]);
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int x = 4 * s + e, kb = x >> 4, r = x & 15;
+      const float p = __builtin_amdgcn_exp2f(cur[kb][r] * c2 - muse);
+      cur[kb][r] = p;
+      rs += p;
+    }
+    nxs[1] = mfma32(op[s & 1][1], qr[s], nxs[1]);
+#pragma unroll
+    for (int e = 2; e < 4; ++e) {
+      const int x = 4 * s + e, kb = x >> 4, r = x & 15;
+      const float p = __builtin_amdgcn_exp2f(cur[kb][r] * c2 - muse);
+      cur[kb][r] = p;
+      rs += p;
+    }
+  }
+  return rs;
+}
+
 // s_waitcnt lgkmcnt(0) (gfx9 encoding; vmcnt and expcnt left unlimited)
 __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 constexpr int kSpinLimit = 1 << 22;
@@ -292,8 +383,8 @@ constexpr int kSpinLimit = 1 << 22;
 // the exact per-block max test decides every tile of L_t in the loop.
 template <bool kExact>
 __global__ __launch_bounds__(kThreads, 1) void k_attn_fwd(AttnArgs a) {
-  // two K/V tile buffers of 2 x 16 KB
-  __shared__ __attribute__((aligned(1024))) char tiles[2][2 * kTileBytes];
+  // three K/V tile buffers of 2 x 16 KB (the exact mode uses two)
+  __shared__ __attribute__((aligned(1024))) char tiles[3][2 * kTileBytes];
   __shared__ int wave_maxrow[kWaves];
   __shared__ int wave_ntiles[kWaves];
   // exact mode: per-wave mailbox, (step + 1) << 32 | bits of the wave's
@@ -387,6 +478,60 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_fwd(AttnArgs a) {
     return load_rows(kbase, vbase, key_of(s, rg, raw), a.N, lane);
   };
 
+  int n_visit = 0;  // exact mode: tiles attended
+  if constexpr (!kExact) {
+    // Software pipeline, one step per tile s: the QK of tile s + 1 (buffer
+    // (s + 1) % 3) is issued between the row rescale and the exponentials
+    // of tile s, then the PV of tile s (buffer s % 3), then tile s + 2's
+    // rows (loaded during step s - 1) go to buffer (s + 2) % 3, which held
+    // tile s - 1, and the loads of tile s + 3's rows and tile s + 4's
+    // indices are issued. One barrier per step. A wave whose block has
+    // stopped runs the same instructions as a no-op.
+    {
+      const Staged r0 = stage(0, *key_src(0, rg));
+      const Staged r1 = stage(1, *key_src(1, rg));
+      store_rows(tiles[0], tiles[0] + kTileBytes, r0, sta);
+      store_rows(tiles[1], tiles[1] + kTileBytes, r1, sta);
+    }
+    Staged nxt = stage(2, *key_src(2, rg));
+    int raw = *key_src(3, rg);
+    __syncthreads();
+    f32x16 sa[2], sb[2];
+    qk_tile(tiles[0], qr, sa, ra);
+    auto body = [&](int s, f32x16 (&cur)[2], f32x16 (&nxs)[2]) {
+      const bool local = s < ndiag;
+      if (local) {
+        // key j0 + off of the tile is masked iff off > iq - j0 - 4 lh
+        const int lim = iq - (seg0 + s * kBlock) - 4 * lh;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int off = kb * 32 + 8 * (r >> 2) + (r & 3);
+            cur[kb][r] = off > lim ? -INFINITY : cur[kb][r];
+          }
+      }
+      const bool act = valid && (local || (s - ndiag) < nI);
+      const float muse = row_rescale(cur, oacc, m, l, a.c2, act);
+      __builtin_amdgcn_sched_barrier(0);
+      const float rs = qk_exp(tiles[(s + 1) % 3], qr, nxs, cur, a.c2, muse, ra);
+      l += sum_xor32(rs);
+      __builtin_amdgcn_sched_barrier(0);
+      pv_tile(tiles[s % 3] + kTileBytes, cur, oacc, ra);
+      char* const nb = tiles[(s + 2) % 3];
+      store_rows(nb, nb + kTileBytes, nxt, sta);
+      nxt = stage(s + 3, raw);
+      raw = *key_src(s + 4, rg);
+      wait_lgkm0();
+      __builtin_amdgcn_s_barrier();
+    };
+    int s = 0;
+    for (; s + 1 < nsteps; s += 2) {
+      body(s, sa, sb);
+      body(s + 1, sb, sa);
+    }
+    if (s < nsteps) body(s, sa, sb);
+  } else {
   // prologue: step 0's rows into buffer 0, step 1's rows into registers,
   // indices of step 2
   {
@@ -398,7 +543,6 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_fwd(AttnArgs a) {
   int raw = *key_src(2, rg);
   __syncthreads();
 
-  int n_visit = 0;  // exact mode: tiles attended
   for (int s = 0; s < nsteps; ++s) {
     const char* Kt = tiles[s & 1];
     const char* Vt = Kt + kTileBytes;
@@ -460,6 +604,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_fwd(AttnArgs a) {
     }
     wait_lgkm0();
     __builtin_amdgcn_s_barrier();
+  }
   }
   __builtin_amdgcn_s_waitcnt(0);  // index loads of steps never taken
 

@@ -30,14 +30,12 @@
 
 namespace sa {
 
-namespace {
-
 constexpr int kScanBlocks = 128;  // query blocks per scan workgroup
 constexpr int kScanThreads = 4 * kScanBlocks;
 constexpr int kScanTiles = 32;    // tiles whose key sums sit in LDS at once
 
 // Adds the 8 bfloat16 of one 16-byte load to s[0..7].
-__device__ __forceinline__ void add_bf16x8(float (&s)[8], uint4 w) {
+static __device__ __forceinline__ void add_bf16x8(float (&s)[8], uint4 w) {
   s[0] += bf16_bits_to_f32(w.x & 0xffffu);
   s[1] += bf16_bits_to_f32(w.x >> 16);
   s[2] += bf16_bits_to_f32(w.y & 0xffffu);
@@ -53,7 +51,7 @@ __device__ __forceinline__ void add_bf16x8(float (&s)[8], uint4 w) {
 // l / 16 + 4, ... (ascending), then the four row groups are added across
 // lanes (l ^ 16, then l ^ 32). Lanes 0..15 return dims 8 (l % 16) .. + 7;
 // every lane of a 16-lane column ends with the same bits.
-__device__ __forceinline__ void sum_rows64(const uint16_t* base,
+static __device__ __forceinline__ void sum_rows64(const uint16_t* base,
                                            int row_of_lane, int lane,
                                            float (&s)[8]) {
   const int c = lane & 15, rg = lane >> 4;
@@ -77,14 +75,14 @@ __device__ __forceinline__ void sum_rows64(const uint16_t* base,
 
 // Sum over the four lanes of an aligned quad (DPP quad permutations); the
 // two additions pair equal operands, so all four lanes end with equal bits.
-__device__ __forceinline__ float quad_sum(float x) {
+static __device__ __forceinline__ float quad_sum(float x) {
   x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF,
                                                0xF, true));  // [1,0,3,2]
   x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF,
                                                0xF, true));  // [2,3,0,1]
   return x;
 }
-__device__ __forceinline__ int quad_sum_int(int x) {
+static __device__ __forceinline__ int quad_sum_int(int x) {
   x += __builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, true);
   x += __builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, true);
   return x;
@@ -242,8 +240,6 @@ __global__ __launch_bounds__(kScanThreads) void k_stop_scan(StopArgs a) {
   }
   if (valid && dq == 0) *nout = n;
 }
-
-}  // namespace
 
 hipError_t launch_block_qsum(const PlanDims& d, const uint16_t* q,
                              const int32_t* pi_q, float* qsum, hipStream_t s) {

@@ -52,6 +52,10 @@ CASES = [
      O.SA_SEGMENT_KV),
     ("s4096_merge_sort_n8192", _spec(1, 2, 1, 8192, 30, n_vert=64,
                                      window=128), 4096, (0.02,), 0),
+    # 4 query heads x 64 blocks per segment: the stop scan splits a segment's
+    # 256 blocks over two workgroups and its 64 local blocks over two chunks
+    ("g4_s4096_two_scan_chunks", _spec(1, 4, 1, 8192, 39, n_vert=64,
+                                       window=128), 4096, (0.02, 0.1), 0),
 ]
 
 

@@ -29,10 +29,10 @@
 //
 // Exact per-block max mode (the BSFA page's test, instead of the stop): every
 // tile of L_t is scored and attended iff the largest logit of the 64 x 64
-// tile reaches the threshold; the two halves of a block hand each other
-// their tile maxima through an LDS mailbox so both decide on the same bits.
-// This mode keeps the plain order per step (QK, row stores and loads,
-// handshake, softmax / PV) over two of the buffers.
+// tile reaches the threshold. Each half of a block posts its maximum of
+// tile s + 1 to LDS right after that tile's QK (one slot per step parity);
+// after the barrier both halves take max(own, other) of the same two
+// values, so they decide on the same bits without waiting for each other.
 //
 // Per wave and 64-key tile:
 //   S^T = K Q^T   : 2 v_mfma_f32_32x32x16_bf16 blocks over d = 128, Q^T
@@ -236,58 +236,6 @@ __device__ __forceinline__ float lane_max(const f32x16 (&sacc)[2]) {
 }
 
 
-// Online softmax update of this lane's query row, then O^T += V^T P^T.
-// m is kept in the exp2 domain (m = reference logit * c2).
-__device__ __forceinline__ void softmax_pv(const char* Vt, f32x16 (&sacc)[2],
-                                           f32x16 (&oacc)[4], float& m,
-                                           float& l, float c2,
-                                           const ReadAddr& ra) {
-  float v = -INFINITY;
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) v = fmaxf(v, sacc[kb][r]);
-  const float mx = max_xor32(v) * c2;
-  // raise the reference only when some row's max exceeds it by > 2^8
-  if (__builtin_amdgcn_ballot_w64(mx > m + kRescaleSlack) != 0) {
-    const float mnew = fmaxf(m, mx);
-    // 0 when m was -inf; 1 when unchanged (also when both are -inf)
-    const float alpha = m == mnew ? 1.f : __builtin_amdgcn_exp2f(m - mnew);
-    l *= alpha;
-#pragma unroll
-    for (int db = 0; db < 4; ++db) oacc[db] *= alpha;
-    m = mnew;
-  }
-  // a row with no visible key yet has only masked (-inf) logits: p = 0
-  const float muse = m == -INFINITY ? 0.f : m;
-  float rs = 0.f;
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float p = __builtin_amdgcn_exp2f(sacc[kb][r] * c2 - muse);
-      sacc[kb][r] = p;
-      rs += p;
-    }
-  l += sum_xor32(rs);
-#pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    const int kb = s >> 1, half = s & 1;
-    bf16x8 pb;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) pb[e] = (__bf16)sacc[kb][8 * half + e];
-#pragma unroll
-    for (int db = 0; db < 4; ++db) {
-      const int id = ((2 * kb + half) * 4 + db) * 2;
-      const char* p = Vt + id * 512 + ra.vofs[db & 1];
-      const s16x4 lo = lds_read_tr16(p);
-      const s16x4 hi = lds_read_tr16(p + 512);
-      const s16x8 cat = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-      oacc[db] = mfma32(__builtin_bit_cast(bf16x8, cat), pb, oacc[db]);
-    }
-  }
-}
-
 // The online softmax of one tile in pieces (row max and rescale here, the
 // exponentials in qk_exp, the PV product in pv_tile), so that the QK MFMAs
 // of the next tile can be interleaved with the exponentials of this one.
@@ -376,20 +324,18 @@ __device__ __forceinline__ float qk_exp(const char* Kt, const bf16x8 (&qr)[8],
 
 // s_waitcnt lgkmcnt(0) (gfx9 encoding; vmcnt and expcnt left unlimited)
 __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
-constexpr int kSpinLimit = 1 << 22;
 
 // kExact = false: each block attends its dense local window and the first
 // n_I tiles of L_t, n_I given (the early stop's stop points). kExact = true:
 // the exact per-block max test decides every tile of L_t in the loop.
 template <bool kExact>
 __global__ __launch_bounds__(kThreads, 1) void k_attn_fwd(AttnArgs a) {
-  // three K/V tile buffers of 2 x 16 KB (the exact mode uses two)
+  // three K/V tile buffers of 2 x 16 KB
   __shared__ __attribute__((aligned(1024))) char tiles[3][2 * kTileBytes];
   __shared__ int wave_maxrow[kWaves];
   __shared__ int wave_ntiles[kWaves];
-  // exact mode: per-wave mailbox, (step + 1) << 32 | bits of the wave's
-  // tile maximum
-  __shared__ unsigned long long mailbox[kWaves];
+  // exact mode: each wave's maximum of the next tile, by step parity
+  __shared__ unsigned tile_max[2][kWaves];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int lq = lane & 31, lh = lane >> 5;
   const int qsub = wave & 3, half = wave >> 2;
@@ -447,7 +393,6 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_fwd(AttnArgs a) {
   if (lane == 0) {
     wave_maxrow[wave] = valid ? myrow : -1;
     wave_ntiles[wave] = nI;
-    if (kExact) mailbox[wave] = 0ull;
   }
   __syncthreads();
   int wgmax = -1, ntiles = 0;
@@ -478,134 +423,79 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_fwd(AttnArgs a) {
     return load_rows(kbase, vbase, key_of(s, rg, raw), a.N, lane);
   };
 
-  int n_visit = 0;  // exact mode: tiles attended
-  if constexpr (!kExact) {
-    // Software pipeline, one step per tile s: the QK of tile s + 1 (buffer
-    // (s + 1) % 3) is issued between the row rescale and the exponentials
-    // of tile s, then the PV of tile s (buffer s % 3), then tile s + 2's
-    // rows (loaded during step s - 1) go to buffer (s + 2) % 3, which held
-    // tile s - 1, and the loads of tile s + 3's rows and tile s + 4's
-    // indices are issued. One barrier per step. A wave whose block has
-    // stopped runs the same instructions as a no-op.
-    {
-      const Staged r0 = stage(0, *key_src(0, rg));
-      const Staged r1 = stage(1, *key_src(1, rg));
-      store_rows(tiles[0], tiles[0] + kTileBytes, r0, sta);
-      store_rows(tiles[1], tiles[1] + kTileBytes, r1, sta);
+  // Software pipeline, one step per tile s: the QK of tile s + 1 (buffer
+  // (s + 1) % 3) is issued between the row rescale and the exponentials of
+  // tile s, then the PV of tile s (buffer s % 3), then tile s + 2's rows
+  // (loaded during step s - 1) go to buffer (s + 2) % 3, which held tile
+  // s - 1, and the loads of tile s + 3's rows and tile s + 4's indices are
+  // issued. One barrier per step. A wave whose block has stopped (or whose
+  // tile the exact test rejects) runs the same instructions as a no-op.
+  {
+    const Staged r0 = stage(0, *key_src(0, rg));
+    const Staged r1 = stage(1, *key_src(1, rg));
+    store_rows(tiles[0], tiles[0] + kTileBytes, r0, sta);
+    store_rows(tiles[1], tiles[1] + kTileBytes, r1, sta);
+  }
+  Staged nxt = stage(2, *key_src(2, rg));
+  int raw = *key_src(3, rg);
+  __syncthreads();
+  f32x16 sa[2], sb[2];
+  qk_tile(tiles[0], qr, sa, ra);
+  int n_visit = 0;     // exact mode: tiles attended
+  float my_max = 0.f;  // exact mode: this half's maximum of the current tile
+  auto body = [&](int s, f32x16 (&cur)[2], f32x16 (&nxs)[2]) {
+    const bool local = s < ndiag;
+    if (local) {
+      // key j0 + off of the tile is masked iff off > iq - j0 - 4 lh
+      const int lim = iq - (seg0 + s * kBlock) - 4 * lh;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int off = kb * 32 + 8 * (r >> 2) + (r & 3);
+          cur[kb][r] = off > lim ? -INFINITY : cur[kb][r];
+        }
     }
-    Staged nxt = stage(2, *key_src(2, rg));
-    int raw = *key_src(3, rg);
-    __syncthreads();
-    f32x16 sa[2], sb[2];
-    qk_tile(tiles[0], qr, sa, ra);
-    auto body = [&](int s, f32x16 (&cur)[2], f32x16 (&nxs)[2]) {
-      const bool local = s < ndiag;
-      if (local) {
-        // key j0 + off of the tile is masked iff off > iq - j0 - 4 lh
-        const int lim = iq - (seg0 + s * kBlock) - 4 * lh;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int off = kb * 32 + 8 * (r >> 2) + (r & 3);
-            cur[kb][r] = off > lim ? -INFINITY : cur[kb][r];
-          }
-      }
-      const bool act = valid && (local || (s - ndiag) < nI);
+    bool act = valid && (local || (s - ndiag) < nI);
+    if (kExact && !local) {
+      // exact max test of tile s: both halves take max(own, other) of the
+      // maxima posted with the tile's logits, before the last barrier
+      const float other = __uint_as_float(tile_max[s & 1][wave ^ 4]);
+      const bool take = fmaxf(my_max, other) >= a.exact_thr;
+      n_visit += (act && take) ? 1 : 0;
+      act = act && take;
+    }
+    if (kExact && !act) {
+      // a tile the exact test rejects (most of them): only the next QK
+      qk_tile(tiles[(s + 1) % 3], qr, nxs, ra);
+    } else {
       const float muse = row_rescale(cur, oacc, m, l, a.c2, act);
       __builtin_amdgcn_sched_barrier(0);
-      const float rs = qk_exp(tiles[(s + 1) % 3], qr, nxs, cur, a.c2, muse, ra);
+      const float rs =
+          qk_exp(tiles[(s + 1) % 3], qr, nxs, cur, a.c2, muse, ra);
       l += sum_xor32(rs);
       __builtin_amdgcn_sched_barrier(0);
       pv_tile(tiles[s % 3] + kTileBytes, cur, oacc, ra);
-      char* const nb = tiles[(s + 2) % 3];
-      store_rows(nb, nb + kTileBytes, nxt, sta);
-      nxt = stage(s + 3, raw);
-      raw = *key_src(s + 4, rg);
-      wait_lgkm0();
-      __builtin_amdgcn_s_barrier();
-    };
-    int s = 0;
-    for (; s + 1 < nsteps; s += 2) {
-      body(s, sa, sb);
-      body(s + 1, sb, sa);
     }
-    if (s < nsteps) body(s, sa, sb);
-  } else {
-  // prologue: step 0's rows into buffer 0, step 1's rows into registers,
-  // indices of step 2
-  {
-    const Staged r0 = stage(0, *key_src(0, rg));
-    store_rows(tiles[0], tiles[0] + kTileBytes, r0, sta);
-  }
-  Staged nxt = {};
-  if (nsteps > 1) nxt = stage(1, *key_src(1, rg));
-  int raw = *key_src(2, rg);
-  __syncthreads();
-
-  for (int s = 0; s < nsteps; ++s) {
-    const char* Kt = tiles[s & 1];
-    const char* Vt = Kt + kTileBytes;
-
-    // local block (s < ndiag): exact causal attention of the rows that see
-    // any of its keys; sparse tile: attention up to the stop point (exact
-    // mode: the max test first)
-    const bool local = s < ndiag;
-    const int j0 = seg0 + s * kBlock;
-    const bool compute = valid && (local ? myrow >= j0 : (s - ndiag) < nI);
-    typedef __attribute__((address_space(3))) volatile unsigned long long
-        lds_u64;
-    lds_u64* box = (lds_u64*)mailbox;
-    float ps = 0.f;
-    if (compute) {
-      qk_tile(Kt, qr, sacc, ra);
-      if (kExact && !local) {
-        // the half's tile maximum, for the other half of the block
-        ps = wave_max(lane_max(sacc));
-        if (lane == 0)
-          box[wave] = ((unsigned long long)(s + 1) << 32) | __float_as_uint(ps);
-      }
+    if (kExact) {
+      // this half's maximum of tile s + 1, for the other half (the slot of
+      // step s + 1's parity; the other slot is being read this step)
+      my_max = wave_max(lane_max(nxs));
+      if (lane == 0) tile_max[(s + 1) & 1][wave] = __float_as_uint(my_max);
     }
-    // step s + 1's rows (loaded during step s - 1) -> the other buffer,
-    // which held step s - 1's tile (read by every wave before the last
-    // barrier); then the loads of step s + 2's rows and of step s + 3's
-    // indices
-    store_rows(tiles[(s + 1) & 1], tiles[(s + 1) & 1] + kTileBytes, nxt,
-               sta);
-    nxt = stage(s + 2, raw);
-    raw = *key_src(s + 3, rg);
-    if (compute) {
-      bool take = true;
-      if (local) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int jk = j0 + kb * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
-            if (jk > iq) sacc[kb][r] = -INFINITY;
-          }
-      } else if (kExact) {
-        // wait for the other half's maximum of this step (bounded); both
-        // halves take max of the same two values
-        unsigned long long other;
-        int spins = 0;
-        while (true) {
-          other = box[wave ^ 4];
-          if ((other >> 32) == (unsigned long long)(s + 1) ||
-              ++spins >= kSpinLimit)
-            break;
-          __builtin_amdgcn_s_sleep(1);
-        }
-        const float po = __uint_as_float((uint32_t)other);
-        take = fmaxf(ps, po) >= a.exact_thr;
-        n_visit += take ? 1 : 0;
-      }
-      if (take) softmax_pv(Vt, sacc, oacc, m, l, a.c2, ra);
-    }
+    char* const nb = tiles[(s + 2) % 3];
+    store_rows(nb, nb + kTileBytes, nxt, sta);
+    nxt = stage(s + 3, raw);
+    raw = *key_src(s + 4, rg);
     wait_lgkm0();
     __builtin_amdgcn_s_barrier();
+  };
+  int s = 0;
+  for (; s + 1 < nsteps; s += 2) {
+    body(s, sa, sb);
+    body(s + 1, sb, sa);
   }
-  }
+  if (s < nsteps) body(s, sa, sb);
   __builtin_amdgcn_s_waitcnt(0);  // index loads of steps never taken
 
   // ---- epilogue: normalise, round to bf16, scatter to the original rows.

@@ -235,7 +235,8 @@ __global__ __launch_bounds__(256) void k_chunk_sort(
   for (int kk = 2; kk <= np2; kk <<= 1) {
     for (int j = kk >> 1; j > 0; j >>= 1) {
       for (int p = threadIdx.x; p < (np2 >> 1); p += 256) {
-        const int i = (p / j) * 2 * j + (p % j);
+        // j is a power of two: i = 2 j (p / j) + p % j
+        const int i = ((p & ~(j - 1)) << 1) | (p & (j - 1));
         cmp_swap(key, idx, i, i + j, (i & kk) == 0);
       }
       __syncthreads();
@@ -458,7 +459,8 @@ __global__ __launch_bounds__(256) void k_segment_tiles(
   for (int kk = 2; kk <= np2; kk <<= 1) {
     for (int j = kk >> 1; j > 0; j >>= 1) {
       for (int p = threadIdx.x; p < (np2 >> 1); p += 256) {
-        const int i = (p / j) * 2 * j + (p % j);
+        // j is a power of two: i = 2 j (p / j) + p % j
+        const int i = ((p & ~(j - 1)) << 1) | (p & (j - 1));
         cmp_swap(key, idx, i, i + j, (i & kk) == 0);
       }
       __syncthreads();

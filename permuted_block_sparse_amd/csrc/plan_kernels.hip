@@ -171,6 +171,27 @@ __global__ __launch_bounds__(128) void k_contrast(
 }
 
 // Query stripe score u_i = fx(q_i) . C_seg(i) (C_0 = 0, so u = 0 there).
+// int64 sum of the 16 lanes of each aligned 16-lane row, in lane 15 of the
+// row (DPP row shifts; integer addition, so the order does not matter).
+__device__ __forceinline__ int64_t row16_sum_i64(int64_t v) {
+#pragma unroll
+  for (int sh = 1; sh < 16; sh <<= 1) {
+    const int lo = (int)(uint32_t)(uint64_t)v;
+    const int hi = (int)(uint32_t)((uint64_t)v >> 32);
+    // row_shr:sh (0x110 + sh); lanes below the shift read 0
+    const int slo = sh == 1 ? __builtin_amdgcn_update_dpp(0, lo, 0x111, 0xF, 0xF, false)
+                  : sh == 2 ? __builtin_amdgcn_update_dpp(0, lo, 0x112, 0xF, 0xF, false)
+                  : sh == 4 ? __builtin_amdgcn_update_dpp(0, lo, 0x114, 0xF, 0xF, false)
+                            : __builtin_amdgcn_update_dpp(0, lo, 0x118, 0xF, 0xF, false);
+    const int shi = sh == 1 ? __builtin_amdgcn_update_dpp(0, hi, 0x111, 0xF, 0xF, false)
+                  : sh == 2 ? __builtin_amdgcn_update_dpp(0, hi, 0x112, 0xF, 0xF, false)
+                  : sh == 4 ? __builtin_amdgcn_update_dpp(0, hi, 0x114, 0xF, 0xF, false)
+                            : __builtin_amdgcn_update_dpp(0, hi, 0x118, 0xF, 0xF, false);
+    v += (int64_t)(((uint64_t)(uint32_t)shi << 32) | (uint32_t)slo);
+  }
+  return v;
+}
+
 __global__ __launch_bounds__(256) void k_query_score(
     const uint16_t* __restrict__ q, const int64_t* __restrict__ contrast,
     int64_t* __restrict__ u, int Hq, int Hkv, int N, int S, int T, int nwg) {
@@ -181,18 +202,26 @@ __global__ __launch_bounds__(256) void k_query_score(
   const int row0 = w * kScoreRows;
   const int rows = min(kScoreRows, N - row0);
   const uint16_t* base = q + ((size_t)bh * N + row0) * kHeadDim + c * 8;
+  // this lane's 8 entries of C_t, reloaded when the segment changes
+  int t_loaded = -1;
+  int64_t cv[8];
   for (int p = 0; p * 16 < rows; ++p) {
     const int r = rr + 16 * p;
     const int t = (row0 + r) / S;
-    const int64_t* cv = contrast + ((size_t)bg * T + t) * kHeadDim + c * 8;
+    if (t != t_loaded) {
+      const int64_t* src = contrast + ((size_t)bg * T + t) * kHeadDim + c * 8;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) cv[e] = src[e];
+      t_loaded = t;
+    }
     uint4 wv = *reinterpret_cast<const uint4*>(base + (size_t)r * kHeadDim);
     int32_t f[8];
     fixed_point8(wv, f);
     int64_t dot = 0;
 #pragma unroll
     for (int e = 0; e < 8; ++e) dot += (int64_t)f[e] * cv[e];
-    dot = sum16_i64(dot);
-    if (c == 0) u[(size_t)bh * N + row0 + r] = dot;
+    dot = row16_sum_i64(dot);
+    if (c == 15) u[(size_t)bh * N + row0 + r] = dot;
   }
 }
 

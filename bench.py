@@ -209,6 +209,10 @@ def main():
                  "visited_local_tiles": diag_tiles,
                  "dense_equiv_tflops": round(dense_flop / attn_med / 1e9, 1),
                  "visited_tile_tflops": round(achieved, 1)},
+        "plan_bytes": plan_kernel_bytes(
+            B, Hq, Hkv, N, S, d,
+            scan_tiles_read(n_I, B, Hq, Hkv, N, S) if tau > 0 else 0,
+            scanning=tau > 0),
     }
     traffic = None
     try:
@@ -234,6 +238,86 @@ def main():
         result["cpu_baseline"] = cpu_baseline(cfg, q, k, v, S, tau,
                                               nb_total=B * Hq * nb)
     print(json.dumps(result), flush=True)
+
+
+def scan_tiles_read(n_I, B, Hq, Hkv, N, S, chunk=32):
+    """Key tiles of L_t whose sums the stop scan gathers: one workgroup per
+    (b, KV head, segment t >= 1) reads L_t in chunks of 32 tiles until every
+    block of its G heads has stopped (a block that never stops reads all
+    t S / 64 tiles)."""
+    T, bps, G = N // S, S // 64, Hq // Hkv
+    mx = n_I.reshape(B, Hkv, G, T, bps).max(axis=(2, 4))  # (B, Hkv, T)
+    total = 0
+    for t in range(1, T):
+        ntl = t * bps
+        m = mx[:, :, t]
+        total += int(np.minimum((m // chunk + 1) * chunk, ntl).sum())
+    return total
+
+
+def plan_kernel_bytes(B, Hq, Hkv, N, S, d, scan_tiles, scanning=True):
+    """Algorithmic HBM bytes of each planner kernel in one plan: every
+    operand read once, every result written once; gathers count the rows
+    and index entries they fetch. Returns {kernel: {"bytes": per plan,
+    "dispatches": per plan}}; the two chunk-sort dispatches are told apart
+    by their workgroup count."""
+    T, nb, bps = N // S, N // 64, S // 64
+    row = 2 * d
+    qb, kb = B * Hq * N * row, B * Hkv * N * row
+    npc = -(-N // 1024)
+    nrc = -(-N // 4096)
+    part = B * Hq * npc * d * 8
+    out = {}
+    out["k_pool_q"] = qb + part
+    out["k_pool_reduce"] = part + B * Hkv * d * 8
+    out["k_key_score"] = (kb + B * Hkv * d * 8 + B * Hkv * N * 8
+                          + B * Hkv * nb * d * 4)
+    out["k_segment_sum"] = B * Hkv * nb * d * 4 + B * Hkv * T * d * 8
+    out["k_contrast"] = (B * Hkv * (T - 1) * 64 * (row + 4)
+                         + 2 * B * Hkv * T * d * 8)
+    out["k_query_score"] = qb + B * Hkv * T * d * 8 + B * Hq * N * 8
+    res = {k_: {"bytes": v_, "dispatches": 1} for k_, v_ in out.items()}
+
+    def sort(name, n_seg, seglen, score_b):
+        chunk = min(seglen, 4096)
+        nch = -(-seglen // chunk)
+        n = n_seg * seglen
+        passes = 0
+        w = chunk
+        while w < seglen:
+            passes += 1
+            w *= 2
+        # chunk sort: scores in; keys + indices out (indices only when one
+        # chunk holds the segment); each merge pass: keys + indices in and
+        # out (indices only from the last pass)
+        res[f"k_chunk_sort[{name}]"] = {
+            "bytes": n * (score_b + (4 if passes == 0 else 12)),
+            "dispatches": 1, "workgroups": n_seg * nch}
+        return passes, n
+
+    pk, nk = sort("pi_K", B * Hkv, N, 8)
+    pq, nq = sort("pi_Q", B * Hq * T, S, 8)
+    mb = sum(n * (24 * (p - 1) + 16) for p, n in ((pk, nk), (pq, nq)) if p)
+    if pk + pq:
+        res["k_merge_pass"] = {"bytes": mb, "dispatches": pk + pq}
+    cnt = B * Hkv * nrc * T * 4
+    L_bytes = B * Hkv * S * T * (T - 1) // 2 * 4
+    res["k_restrict_count"] = {"bytes": B * Hkv * N * 4 + cnt, "dispatches": 1}
+    res["k_restrict_scan"] = {"bytes": 2 * cnt, "dispatches": 1}
+    res["k_restrict_write"] = {"bytes": B * Hkv * N * 4 + cnt + L_bytes,
+                               "dispatches": 1}
+    res["k_block_qsum"] = {"bytes": B * Hq * N * 4 + qb + B * Hq * nb * d * 4,
+                           "dispatches": 1}
+    # blocks that scan (t >= 1; none when a fixed count decides): their
+    # query sums and pi_Q rows, the local segment's keys once per (b, KV
+    # head, t), the gathered tiles' keys and L entries; n_I written
+    sb = B * Hq * (T - 1) * bps if scanning else 0
+    local = B * Hkv * (T - 1) * S * row if scanning else 0
+    res["k_stop_scan"] = {
+        "bytes": (sb * (d * 4 + 64 * 4) + local
+                  + scan_tiles * 64 * (row + 4) + B * Hq * nb * 4),
+        "dispatches": 1, "scan_tiles": scan_tiles}
+    return res
 
 
 def extras(args, cfg, q, k, v, tq, tk, tv, pl, out, S, tau, timed):

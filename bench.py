@@ -227,7 +227,7 @@ def main():
         "bound": "mfma", "achieved": round(achieved, 2),
         "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
         "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
-        "traffic": traffic, "kernel": "k_attn_fwd",
+        "traffic": traffic, "kernel": "k_attn_fwd<kFastRef>",
         "flop_per_launch": flop_launch,
         "avg_launch_ms": round(attn_mean, 4)}
 

@@ -38,9 +38,14 @@
 //   S^T = K Q^T   : 2 v_mfma_f32_32x32x16_bf16 blocks over d = 128, Q^T
 //                   operands held in registers for the whole run;
 //   online softmax: one query row per lane pair (lane, lane ^ 32), fp32,
-//                   exp2 domain; the running max is raised only when a row's
-//                   max exceeds it by more than 2^8 (exact: o = acc / l for
-//                   any reference);
+//                   exp2 domain; o = acc / l holds for any reference, so
+//                   the reference is raised only when p values could pass
+//                   2^8. Rows provably bounded (the logit bound |q| max |k|
+//                   kappa log2(e) within 120 of the first tile's maximum,
+//                   so no p can overflow) skip the per-tile row maximum
+//                   and test the lane's tile sum instead (a sum above 2^8
+//                   divides the row by its largest p); other workgroups take
+//                   the row maximum of every tile (a second launch);
 //   O^T += V^T P^T: V^T A operands via ds_read_tr16_b64 transposed reads,
 //                   P^T B operands straight from the S registers.
 //
@@ -71,6 +76,12 @@ constexpr int kTileBytes = kBlock * kHeadDim * 2;  // 16 KB: one K or V tile
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr float kRescaleSlack = 8.0f;               // log2 units
+// A lane's sum of one tile's 32 p values above this means some p may exceed
+// 2^kRescaleSlack (every p > 2^8 lifts the sum above it): rescale.
+constexpr float kRescaleSum = 256.0f;
+// Rows whose logits provably stay below reference + kSafeSpan (log2 units)
+// skip the per-tile row maximum: no p can overflow fp32 before the rescale.
+constexpr float kSafeSpan = 120.0f;
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -262,6 +273,26 @@ __device__ __forceinline__ float row_rescale(const f32x16 (&sacc)[2],
   return !active ? INFINITY : m == -INFINITY ? 0.f : m;
 }
 
+// Row maximum of a tile's logits (both lanes of a row pair), times c2.
+__device__ __forceinline__ float row_max(const f32x16 (&sacc)[2], float c2) {
+  return max_xor32(lane_max(sacc)) * c2;
+}
+
+// p = exp2(s c2 - muse) in place; returns the lane's sum.
+__device__ __forceinline__ float tile_exp(f32x16 (&sacc)[2], float c2,
+                                          float muse) {
+  float rs = 0.f;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float p = __builtin_amdgcn_exp2f(sacc[kb][r] * c2 - muse);
+      sacc[kb][r] = p;
+      rs += p;
+    }
+  return rs;
+}
+
 __device__ __forceinline__ void pv_tile(const char* Vt, const f32x16 (&sacc)[2],
                                         f32x16 (&oacc)[4], const ReadAddr& ra) {
 #pragma unroll
@@ -325,11 +356,21 @@ __device__ __forceinline__ float qk_exp(const char* Kt, const bf16x8 (&qr)[8],
 // s_waitcnt lgkmcnt(0) (gfx9 encoding; vmcnt and expcnt left unlimited)
 __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
-// kExact = false: each block attends its dense local window and the first
-// n_I tiles of L_t, n_I given (the early stop's stop points). kExact = true:
-// the exact per-block max test decides every tile of L_t in the loop.
-template <bool kExact>
+// Three instances. kMaxRef and kFastRef: each block attends its dense local
+// window and the first n_I tiles of L_t, n_I given (the early stop's stop
+// points or a budget). kFastRef raises the online softmax's reference only
+// when p values grow past 2^8; it runs the workgroups whose logits are
+// provably bounded, exits from the others and flags them for the kMaxRef
+// launch that follows, which takes the row maximum of every tile and skips
+// the unflagged workgroups. kExactMax: the exact per-block max test decides
+// every tile of L_t in the loop.
+enum : int { kMaxRef = 0, kFastRef = 1, kExactMax = 2 };
+
+template <int kMode>
 __global__ __launch_bounds__(kThreads, 1) void k_attn_fwd(AttnArgs a) {
+  constexpr bool kExact = kMode == kExactMax;
+  constexpr bool kFast = kMode == kFastRef;
+  if (kMode == kMaxRef && a.wg_flag[blockIdx.x] == 0) return;  // done
   // three K/V tile buffers of 2 x 16 KB
   __shared__ __attribute__((aligned(1024))) char tiles[3][2 * kTileBytes];
   __shared__ int wave_maxrow[kWaves];
@@ -441,21 +482,53 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_fwd(AttnArgs a) {
   __syncthreads();
   f32x16 sa[2], sb[2];
   qk_tile(tiles[0], qr, sa, ra);
+  // causal mask of local step s: key j0 + off of the tile is masked iff
+  // off > iq - j0 - 4 lh
+  auto mask_local = [&](int s, f32x16 (&cur)[2]) {
+    const int lim = iq - (seg0 + s * kBlock) - 4 * lh;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int off = kb * 32 + 8 * (r >> 2) + (r & 3);
+        cur[kb][r] = off > lim ? -INFINITY : cur[kb][r];
+      }
+  };
+  // Tau / budget mode: the online softmax's first reference is the row
+  // maximum of tile 0, the segment's first local block, where every row sees
+  // at least one key (the segment's first).
+  if (!kExact) {
+    mask_local(0, sa);
+    m = row_max(sa, a.c2);
+  }
+  if (kFast) {
+    // The logits of a row are bounded by |q| max_j |k_j| (Cauchy-Schwarz);
+    // within kSafeSpan of the reference no p overflows before the rescale
+    // test. A workgroup with an unbounded row leaves it to kMaxRef.
+    float qn = 0.f;  // |q|^2 of the row, fp32
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float x = (float)qr[s][e];
+        qn = fmaf(x, x, qn);
+      }
+    qn = sum_xor32(qn);
+    // fp32 rounding of both norms and of the MFMA sums: a 2^-10 margin
+    const float bound = sqrtf(qn * a.kmax2[bg]) * a.c2 * (1.f + 1.f / 1024.f);
+    const bool safe = bound - m <= kSafeSpan;  // false for NaN
+    const int unsafe = __syncthreads_or(valid && !safe);
+    if (tid == 0) a.wg_flag[blockIdx.x] = unsafe;
+    if (unsafe) {
+      __builtin_amdgcn_s_waitcnt(0);  // loads issued by the prologue
+      return;
+    }
+  }
   int n_visit = 0;     // exact mode: tiles attended
   float my_max = 0.f;  // exact mode: this half's maximum of the current tile
   auto body = [&](int s, f32x16 (&cur)[2], f32x16 (&nxs)[2]) {
     const bool local = s < ndiag;
-    if (local) {
-      // key j0 + off of the tile is masked iff off > iq - j0 - 4 lh
-      const int lim = iq - (seg0 + s * kBlock) - 4 * lh;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int off = kb * 32 + 8 * (r >> 2) + (r & 3);
-          cur[kb][r] = off > lim ? -INFINITY : cur[kb][r];
-        }
-    }
+    if (local) mask_local(s, cur);
     bool act = valid && (local || (s - ndiag) < nI);
     if (kExact && !local) {
       // exact max test of tile s: both halves take max(own, other) of the
@@ -469,10 +542,25 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_fwd(AttnArgs a) {
       // a tile the exact test rejects (most of them): only the next QK
       qk_tile(tiles[(s + 1) % 3], qr, nxs, ra);
     } else {
-      const float muse = row_rescale(cur, oacc, m, l, a.c2, act);
+      const float muse = kFast ? (act ? m : INFINITY)
+                               : row_rescale(cur, oacc, m, l, a.c2, act);
       __builtin_amdgcn_sched_barrier(0);
-      const float rs =
-          qk_exp(tiles[(s + 1) % 3], qr, nxs, cur, a.c2, muse, ra);
+      float rs = qk_exp(tiles[(s + 1) % 3], qr, nxs, cur, a.c2, muse, ra);
+      if (kFast && __builtin_amdgcn_ballot_w64(rs > kRescaleSum) != 0) {
+        // rare: a p value may exceed 2^8; divide the row by its largest p
+        // (this raises the reference by log2 of it)
+        const float pm = max_xor32(lane_max(cur));
+        if (pm > 1.f) {
+          const float sc = __builtin_amdgcn_rcpf(pm);
+          m += __builtin_amdgcn_logf(pm);
+          l *= sc;
+          rs *= sc;
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb) cur[kb] *= sc;
+#pragma unroll
+          for (int db = 0; db < 4; ++db) oacc[db] *= sc;
+        }
+      }
       l += sum_xor32(rs);
       __builtin_amdgcn_sched_barrier(0);
       pv_tile(tiles[s % 3] + kTileBytes, cur, oacc, ra);
@@ -522,11 +610,18 @@ int attention_blocks_per_wg() { return 4; }
 
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
   const int total = a.n_groups * a.wg_per_group;
-  if (a.exact)
-    hipLaunchKernelGGL(k_attn_fwd<true>, dim3(total), dim3(kThreads), 0, s, a);
-  else
-    hipLaunchKernelGGL(k_attn_fwd<false>, dim3(total), dim3(kThreads), 0, s,
-                       a);
+  if (a.exact) {
+    hipLaunchKernelGGL(k_attn_fwd<kExactMax>, dim3(total), dim3(kThreads), 0,
+                       s, a);
+    return hipGetLastError();
+  }
+  // the bounded workgroups, then (flagged by the first launch) the others
+  hipLaunchKernelGGL(k_attn_fwd<kFastRef>, dim3(total), dim3(kThreads), 0, s,
+                     a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_attn_fwd<kMaxRef>, dim3(total), dim3(kThreads), 0, s,
+                     a);
   return hipGetLastError();
 }
 

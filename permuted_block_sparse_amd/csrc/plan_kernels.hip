@@ -78,13 +78,16 @@ __global__ __launch_bounds__(1024) void k_pool_reduce(
 
 // --------------------------------------------------------------------------
 // Key stripe score v_j = pooled . fx(k_j) (int64) and, on the same pass over
-// K, the per-64-row column sums of fx(k) (int32; |sum| <= 64 * 2^15).
+// K, the per-64-row column sums of fx(k) (int32; |sum| <= 64 * 2^15) and the
+// workgroup's largest squared key norm (fp32; their maximum bounds the
+// attention kernel's logits).
 // --------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_key_score(
     const uint16_t* __restrict__ k, const int64_t* __restrict__ pooled,
-    int64_t* __restrict__ vscore, int32_t* __restrict__ blocksum, int N,
-    int nwg) {
+    int64_t* __restrict__ vscore, int32_t* __restrict__ blocksum,
+    float* __restrict__ kpart, int N, int nwg) {
   __shared__ int32_t red[4][16][kHeadDim];
+  __shared__ float wmax[4];
   const int bg = blockIdx.x / nwg, w = blockIdx.x % nwg;
   const int tid = threadIdx.x, c = tid & 15, rr = tid >> 4;
   const int row0 = w * kScoreRows;
@@ -94,6 +97,7 @@ __global__ __launch_bounds__(256) void k_key_score(
   for (int e = 0; e < 8; ++e) p8[e] = pooled[(size_t)bg * kHeadDim + c * 8 + e];
   const uint16_t* base = k + ((size_t)bg * N + row0) * kHeadDim + c * 8;
   int32_t bs[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  float kn = 0.f;  // largest |k|^2 of this thread's rows
   for (int p = 0; p < 16; ++p) {
     const int r = rr + 16 * p;
     if (p * 16 < rows) {  // uniform over the workgroup
@@ -108,6 +112,18 @@ __global__ __launch_bounds__(256) void k_key_score(
       }
       dot = sum16_i64(dot);
       if (c == 0) vscore[(size_t)bg * N + row0 + r] = dot;
+      const uint32_t wd[4] = {wv.x, wv.y, wv.z, wv.w};
+      float sq = 0.f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float lo = __uint_as_float(wd[e] << 16);
+        const float hi = __uint_as_float(wd[e] & 0xffff0000u);
+        sq = fmaf(lo, lo, sq);
+        sq = fmaf(hi, hi, sq);
+      }
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) sq += __shfl_xor(sq, o);
+      kn = fmaxf(kn, sq);
     }
     if ((p & 3) == 3) {
 #pragma unroll
@@ -117,7 +133,12 @@ __global__ __launch_bounds__(256) void k_key_score(
       }
     }
   }
+#pragma unroll
+  for (int o = 16; o < 64; o <<= 1) kn = fmaxf(kn, __shfl_xor(kn, o));
+  if ((tid & 63) == 0) wmax[tid >> 6] = kn;
   __syncthreads();
+  if (tid == 0)
+    kpart[blockIdx.x] = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
   const int nblk = rows / kBlock;
   for (int i = tid; i < 4 * kHeadDim; i += 256) {
     const int bl = i / kHeadDim, d = i % kHeadDim;
@@ -131,11 +152,23 @@ __global__ __launch_bounds__(256) void k_key_score(
   }
 }
 
-// segsum[b, g, t, :] = sum of fx(k) over segment t.
+// segsum[b, g, t, :] = sum of fx(k) over segment t; the t = 0 workgroup
+// also reduces the key-score workgroups' largest |k|^2 to kmax2[b, g].
 __global__ __launch_bounds__(128) void k_segment_sum(
-    const int32_t* __restrict__ blocksum, int64_t* __restrict__ segsum, int N,
-    int S, int T) {
+    const int32_t* __restrict__ blocksum, int64_t* __restrict__ segsum,
+    const float* __restrict__ kpart, float* __restrict__ kmax2, int N, int S,
+    int T, int nwg) {
   const int bgt = blockIdx.x, bg = bgt / T, t = bgt % T, d = threadIdx.x;
+  if (t == 0) {  // uniform over the workgroup
+    __shared__ float wmax[2];
+    float x = 0.f;
+    for (int i = d; i < nwg; i += 128) x = fmaxf(x, kpart[(size_t)bg * nwg + i]);
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) x = fmaxf(x, __shfl_xor(x, o));
+    if ((d & 63) == 0) wmax[d >> 6] = x;
+    __syncthreads();
+    if (d == 0) kmax2[bg] = fmaxf(wmax[0], wmax[1]);
+  }
   const int nb = S / kBlock;
   const int32_t* p =
       blocksum + ((size_t)bg * (N / kBlock) + (size_t)t * nb) * kHeadDim + d;
@@ -226,9 +259,13 @@ __global__ __launch_bounds__(256) void k_query_score(
 }
 
 // --------------------------------------------------------------------------
-// Segmented argsort by (score descending, index ascending): bitonic sort of
-// chunks of up to 4096 elements in LDS, then merge-path merge passes. The
-// composite keys are unique, so the result does not depend on the algorithm.
+// Segmented argsort by (score descending, index ascending). A workgroup
+// sorts a chunk of up to 4096 elements: each thread sorts E consecutive
+// elements in registers (a bitonic network), then log2(256) merge rounds in
+// LDS double the sorted runs, each thread finding its E outputs of a round
+// by a merge-path search. Longer segments are finished by merge passes over
+// global memory. The composite keys are unique, so the result does not
+// depend on the algorithm.
 // --------------------------------------------------------------------------
 __device__ __forceinline__ void cmp_swap(uint64_t* key, int32_t* idx, int i,
                                          int l, bool up) {
@@ -241,37 +278,122 @@ __device__ __forceinline__ void cmp_swap(uint64_t* key, int32_t* idx, int i,
   }
 }
 
+// Merge-path split of diagonal x of two sorted runs A (la) and B (lb): the
+// number of A elements among the first x outputs.
+__device__ __forceinline__ int merge_split(const uint64_t* KA, const int32_t* IA,
+                                           int la, const uint64_t* KB,
+                                           const int32_t* IB, int lb, int x) {
+  int lo = max(0, x - lb), hi = min(x, la);
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (pair_less(KA[mid], IA[mid], KB[x - 1 - mid], IB[x - 1 - mid]))
+      lo = mid + 1;
+    else
+      hi = mid;
+  }
+  return lo;
+}
+
+// n outputs of the merge of A and B starting at A[i], B[j] (n <= the
+// elements left), into registers.
+template <int E>
+__device__ __forceinline__ void merge_run(const uint64_t* KA, const int32_t* IA,
+                                          int la, const uint64_t* KB,
+                                          const int32_t* IB, int lb, int i,
+                                          int j, uint64_t (&rk)[E],
+                                          int32_t (&ri)[E]) {
+  // heads of both runs; an exhausted (or empty) run's head is a clamped,
+  // in-bounds read that the j >= lb / i < la tests never use
+  auto ca = [&](int v) { return max(min(v, la - 1), 0); };
+  auto cb = [&](int v) { return max(min(v, lb - 1), 0); };
+  uint64_t ha = KA[ca(i)], hb = KB[cb(j)];
+  int32_t hia = IA[ca(i)], hib = IB[cb(j)];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const bool ta = j >= lb || (i < la && pair_less(ha, hia, hb, hib));
+    rk[e] = ta ? ha : hb;
+    ri[e] = ta ? hia : hib;
+    if (ta) {
+      ++i;
+      ha = KA[ca(i)];
+      hia = IA[ca(i)];
+    } else {
+      ++j;
+      hb = KB[cb(j)];
+      hib = IB[cb(j)];
+    }
+  }
+}
+
+template <int E>
 __global__ __launch_bounds__(256) void k_chunk_sort(
     const int64_t* __restrict__ score, int seglen, int rowlen, int chunk,
-    int nch, int np2, uint64_t* __restrict__ okey, int32_t* __restrict__ oidx,
+    int nch, uint64_t* __restrict__ okey, int32_t* __restrict__ oidx,
     int32_t* __restrict__ out) {
-  __shared__ uint64_t key[kSortChunk];
-  __shared__ int32_t idx[kSortChunk];
+  constexpr int n = 256 * E;  // >= the chunk; the rest is padding
+  __shared__ uint64_t key[n];
+  __shared__ int32_t idx[n];
+  const int tid = threadIdx.x;
   const int seg = blockIdx.x / nch, ch = blockIdx.x % nch;
   const int start = ch * chunk;
   const int cnt = min(chunk, seglen - start);
   const size_t gbase = (size_t)seg * seglen + start;
-  for (int i = threadIdx.x; i < np2; i += 256) {
+  for (int i = tid; i < n; i += 256) {
     if (i < cnt) {
       key[i] = desc_key(score[gbase + i]);
       idx[i] = (int32_t)((gbase + i) % (size_t)rowlen);
-    } else {
+    } else {  // after every real element
       key[i] = ~0ull;
       idx[i] = 0x7fffffff;
     }
   }
   __syncthreads();
-  for (int kk = 2; kk <= np2; kk <<= 1) {
-    for (int j = kk >> 1; j > 0; j >>= 1) {
-      for (int p = threadIdx.x; p < (np2 >> 1); p += 256) {
-        // j is a power of two: i = 2 j (p / j) + p % j
-        const int i = ((p & ~(j - 1)) << 1) | (p & (j - 1));
-        cmp_swap(key, idx, i, i + j, (i & kk) == 0);
-      }
-      __syncthreads();
-    }
+  // this thread's E elements, sorted in registers
+  uint64_t rk[E];
+  int32_t ri[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    rk[e] = key[tid * E + e];
+    ri[e] = idx[tid * E + e];
   }
-  for (int i = threadIdx.x; i < cnt; i += 256) {
+#pragma unroll
+  for (int kk = 2; kk <= E; kk <<= 1)
+#pragma unroll
+    for (int j = kk >> 1; j > 0; j >>= 1)
+#pragma unroll
+      for (int i = 0; i < E; ++i) {
+        const int l = i ^ j;
+        if (l > i && pair_less(rk[l], ri[l], rk[i], ri[i]) == ((i & kk) == 0)) {
+          const uint64_t tk = rk[i]; rk[i] = rk[l]; rk[l] = tk;
+          const int32_t ti = ri[i]; ri[i] = ri[l]; ri[l] = ti;
+        }
+      }
+  // merge rounds: runs of w become runs of 2 w (every run is full: n is a
+  // power of two)
+  for (int w = E; w < n; w <<= 1) {
+    __syncthreads();  // everyone has read the previous runs
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      key[tid * E + e] = rk[e];
+      idx[tid * E + e] = ri[e];
+    }
+    __syncthreads();
+    const int o = tid * E;
+    const int a0 = o & ~(2 * w - 1);
+    const uint64_t* KA = key + a0;
+    const int32_t* IA = idx + a0;
+    const int x = o - a0;
+    const int i = merge_split(KA, IA, w, KA + w, IA + w, w, x);
+    merge_run<E>(KA, IA, w, KA + w, IA + w, w, i, x - i, rk, ri);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    key[tid * E + e] = rk[e];
+    idx[tid * E + e] = ri[e];
+  }
+  __syncthreads();
+  for (int i = tid; i < cnt; i += 256) {
     if (out != nullptr) {
       out[gbase + i] = idx[i];
     } else {
@@ -281,53 +403,98 @@ __global__ __launch_bounds__(256) void k_chunk_sort(
   }
 }
 
-// One merge pass: runs of `width` become runs of 2 width. Each thread emits
-// up to 8 consecutive outputs after a merge-path binary search.
+// One merge pass over global memory: runs of `width` (a multiple of
+// kMergeTile / 2) become runs of 2 width. Workgroup p of a segment emits its
+// outputs [kMergeTile p, kMergeTile (p + 1)): a k-ary merge-path search (128
+// candidates per round and per end) finds where the range starts and ends in
+// the two runs, both input windows go to LDS, each thread merges 8 outputs
+// from there, and the outputs leave in coalesced rows.
+constexpr int kMergeTile = 2048;
+
 __global__ __launch_bounds__(256) void k_merge_pass(
     const uint64_t* __restrict__ ikey, const int32_t* __restrict__ iidx,
     uint64_t* __restrict__ okey, int32_t* __restrict__ oidx,
-    int32_t* __restrict__ out, int n_seg, int seglen, int width) {
-  const long long tpos = (long long)blockIdx.x * 256 + threadIdx.x;
-  const int per_seg = (seglen + 7) / 8;
-  if (tpos >= (long long)n_seg * per_seg) return;
-  const int seg = (int)(tpos / per_seg);
-  const int o = (int)(tpos % per_seg) * 8;
-  const int pair = o / (2 * width);
-  const int a0 = pair * 2 * width;
-  const int a1 = min(a0 + width, seglen);
-  const int b1 = min(a0 + 2 * width, seglen);
+    int32_t* __restrict__ out, int seglen, int width, int tiles_per_seg) {
+  __shared__ uint64_t sk[kMergeTile];
+  __shared__ int32_t si[kMergeTile];
+  __shared__ int s_lo[2], s_hi[2], s_cnt[4];
+  const int tid = threadIdx.x, hsel = tid >> 7, t = tid & 127;
+  const int seg = blockIdx.x / tiles_per_seg;
+  const int o0 = (blockIdx.x % tiles_per_seg) * kMergeTile;
+  const int o1 = min(o0 + kMergeTile, seglen);
+  const int a0 = (o0 / (2 * width)) * 2 * width;  // o1 - 1 is in this pair
+  const int a1 = min(a0 + width, seglen), b1 = min(a0 + 2 * width, seglen);
   const int la = a1 - a0, lb = b1 - a1;
-  const int x = o - a0;  // outputs of this pair before ours
   const size_t base = (size_t)seg * seglen;
   const uint64_t* KA = ikey + base + a0;
   const int32_t* IA = iidx + base + a0;
   const uint64_t* KB = ikey + base + a1;
   const int32_t* IB = iidx + base + a1;
-  int lo = max(0, x - lb), hi = min(x, la);
-  while (lo < hi) {
-    const int mid = (lo + hi) >> 1;
-    // take A[mid] before B[x-1-mid]?
-    if (pair_less(KA[mid], IA[mid], KB[x - 1 - mid], IB[x - 1 - mid]))
-      lo = mid + 1;
-    else
-      hi = mid;
+
+  // splits of diagonals o0 - a0 (threads 0..127) and o1 - a0 (128..255);
+  // each round samples 128 points of [lo, hi), where the predicate "A[m]
+  // comes before B[x - 1 - m]" is true below the split and false above
+  const int x = (hsel ? o1 : o0) - a0;
+  if (t == 0) {
+    s_lo[hsel] = max(0, x - lb);
+    s_hi[hsel] = min(x, la);
   }
-  int i = lo, j = x - lo;
-  const int n_out = min(8, la + lb - x);
-  for (int e = 0; e < n_out; ++e) {
-    bool take_a;
-    if (i >= la) take_a = false;
-    else if (j >= lb) take_a = true;
-    else take_a = pair_less(KA[i], IA[i], KB[j], IB[j]);
-    const uint64_t kv = take_a ? KA[i] : KB[j];
-    const int32_t iv = take_a ? IA[i] : IB[j];
-    if (take_a) ++i; else ++j;
-    const size_t dst = base + o + e;
+  __syncthreads();
+  for (;;) {
+    const int lo = s_lo[hsel], hi = s_hi[hsel];
+    const int R = hi - lo;
+    const int m = lo + (int)(((long long)R * t) >> 7);  // in [lo, hi) if R > 0
+    const bool pr =
+        R > 0 && pair_less(KA[m], IA[m], KB[x - 1 - m], IB[x - 1 - m]);
+    const unsigned long long bal = __ballot(pr);
+    if ((tid & 63) == 0) s_cnt[tid >> 6] = __popcll(bal);
+    __syncthreads();
+    const int c = s_cnt[2 * hsel] + s_cnt[2 * hsel + 1];  // true prefix
+    __syncthreads();  // every thread has read lo, hi and the counts
+    if (R > 0) {
+      if (t == c - 1) s_lo[hsel] = m + 1;
+      if (t == c) s_hi[hsel] = m;
+    }
+    __syncthreads();
+    if (s_lo[0] == s_hi[0] && s_lo[1] == s_hi[1]) break;  // uniform
+  }
+  const int ia0 = s_lo[0], ia1 = s_lo[1];
+  const int ib0 = (o0 - a0) - ia0, ib1 = (o1 - a0) - ia1;
+  const int na = ia1 - ia0, nb = ib1 - ib0;  // na + nb = o1 - o0
+  for (int i = tid; i < na; i += 256) {
+    sk[i] = KA[ia0 + i];
+    si[i] = IA[ia0 + i];
+  }
+  for (int i = tid; i < nb; i += 256) {
+    sk[na + i] = KB[ib0 + i];
+    si[na + i] = IB[ib0 + i];
+  }
+  __syncthreads();
+  uint64_t rk[8];
+  int32_t ri[8];
+  const int y = 8 * tid;
+  const int n_out = o1 - o0;
+  if (y < n_out) {
+    const int i = merge_split(sk, si, na, sk + na, si + na, nb, y);
+    merge_run<8>(sk, si, na, sk + na, si + na, nb, i, y - i, rk, ri);
+  }
+  __syncthreads();
+  if (y < n_out) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      if (y + e < n_out) {
+        sk[y + e] = rk[e];
+        si[y + e] = ri[e];
+      }
+    }
+  }
+  __syncthreads();
+  for (int i = tid; i < n_out; i += 256) {
     if (out != nullptr) {
-      out[dst] = iv;
+      out[base + o0 + i] = si[i];
     } else {
-      okey[dst] = kv;
-      oidx[dst] = iv;
+      okey[base + o0 + i] = sk[i];
+      oidx[base + o0 + i] = si[i];
     }
   }
 }
@@ -402,12 +569,18 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* wsum,
   return before + x - v;
 }
 
+// One workgroup per (b, g, chunk, part): the chunk's entries go to the lists
+// L_t with t = 1 + part, 1 + part + split, ... (interleaved, so the parts
+// write about the same amount). Per list, the chunk's surviving entries are
+// compacted in LDS and leave as one contiguous run.
 __global__ __launch_bounds__(256) void k_restrict_write(
     const int32_t* __restrict__ pi_k, const int32_t* __restrict__ cum,
-    int32_t* __restrict__ L, int N, int S, int T, int nrc,
+    int32_t* __restrict__ L, int N, int S, int T, int nrc, int split,
     long long list_len) {
   __shared__ int wsum[4];
-  const int bg = blockIdx.x / nrc, ch = blockIdx.x % nrc;
+  __shared__ int32_t buf[kRestrictChunk];
+  const int part = blockIdx.x % split, bgc = blockIdx.x / split;
+  const int bg = bgc / nrc, ch = bgc % nrc;
   const int start = ch * kRestrictChunk;
   const int n = min(kRestrictChunk, N - start);
   constexpr int kPer = kRestrictChunk / 256;
@@ -421,22 +594,23 @@ __global__ __launch_bounds__(256) void k_restrict_write(
     segv[e] = i < n ? keyv[e] / S : 0x7fffffff;
   }
   int32_t* Lbg = L + (size_t)bg * list_len;
-  for (int t = 1; t < T; ++t) {
+  for (int t = 1 + part; t < T; t += split) {
     int c = 0;
 #pragma unroll
     for (int e = 0; e < kPer; ++e) c += segv[e] < t;
     int total;
-    int pos = block_exclusive_scan(c, wsum, total);
-    pos += cum[((size_t)bg * nrc + ch) * T + t];
-    int32_t* Lt = Lbg + (size_t)S * t * (t - 1) / 2;
-    const int cap = t * S;  // |L_t|; only exceeded if pi_K is no permutation
+    int pos = block_exclusive_scan(c, wsum, total);  // total <= n
 #pragma unroll
     for (int e = 0; e < kPer; ++e) {
-      if (segv[e] < t) {
-        if (pos < cap) Lt[pos] = keyv[e];
-        ++pos;
-      }
+      if (segv[e] < t) buf[pos++] = keyv[e];
     }
+    __syncthreads();
+    const int base = cum[((size_t)bg * nrc + ch) * T + t];
+    int32_t* Lt = Lbg + (size_t)S * t * (t - 1) / 2;
+    const int cap = t * S;  // |L_t|; only exceeded if pi_K is no permutation
+    for (int i = threadIdx.x; i < total; i += 256)
+      if (base + i < cap) Lt[base + i] = buf[i];
+    __syncthreads();  // buf is refilled for the next list
   }
 }
 
@@ -517,16 +691,19 @@ hipError_t launch_pool_reduce(const PlanDims& d, const int64_t* part,
 
 hipError_t launch_key_score(const PlanDims& d, const uint16_t* k,
                             const int64_t* pooled, int64_t* vscore,
-                            int32_t* blocksum, hipStream_t s) {
+                            int32_t* blocksum, float* kpart, hipStream_t s) {
   hipLaunchKernelGGL(k_key_score, dim3(d.B * d.Hkv * d.n_score_wg), dim3(256),
-                     0, s, k, pooled, vscore, blocksum, d.N, d.n_score_wg);
+                     0, s, k, pooled, vscore, blocksum, kpart, d.N,
+                     d.n_score_wg);
   return hipGetLastError();
 }
 
 hipError_t launch_segment_sum(const PlanDims& d, const int32_t* blocksum,
-                              int64_t* segsum, hipStream_t s) {
+                              int64_t* segsum, const float* kpart,
+                              float* kmax2, hipStream_t s) {
   hipLaunchKernelGGL(k_segment_sum, dim3(d.B * d.Hkv * d.T), dim3(kHeadDim), 0,
-                     s, blocksum, segsum, d.N, d.S, d.T);
+                     s, blocksum, segsum, kpart, kmax2, d.N, d.S, d.T,
+                     d.n_score_wg);
   return hipGetLastError();
 }
 
@@ -555,22 +732,28 @@ hipError_t launch_segmented_argsort(const int64_t* score, int n_seg,
                                     hipStream_t s) {
   const int chunk = seglen < kSortChunk ? seglen : kSortChunk;
   const int nch = (seglen + chunk - 1) / chunk;
-  int np2 = 1;
+  int np2 = 256;  // 256 threads x E elements, E a power of two <= 16
   while (np2 < chunk) np2 <<= 1;
   const bool single = nch == 1;
-  hipLaunchKernelGGL(k_chunk_sort, dim3(n_seg * nch), dim3(256), 0, s, score,
-                     seglen, rowlen, chunk, nch, np2, key_a, idx_a,
-                     single ? out : nullptr);
+  int32_t* o1 = single ? out : nullptr;
+  const dim3 g(n_seg * nch), b(256);
+  switch (np2) {
+    case 256: hipLaunchKernelGGL(k_chunk_sort<1>, g, b, 0, s, score, seglen, rowlen, chunk, nch, key_a, idx_a, o1); break;
+    case 512: hipLaunchKernelGGL(k_chunk_sort<2>, g, b, 0, s, score, seglen, rowlen, chunk, nch, key_a, idx_a, o1); break;
+    case 1024: hipLaunchKernelGGL(k_chunk_sort<4>, g, b, 0, s, score, seglen, rowlen, chunk, nch, key_a, idx_a, o1); break;
+    case 2048: hipLaunchKernelGGL(k_chunk_sort<8>, g, b, 0, s, score, seglen, rowlen, chunk, nch, key_a, idx_a, o1); break;
+    default: hipLaunchKernelGGL(k_chunk_sort<16>, g, b, 0, s, score, seglen, rowlen, chunk, nch, key_a, idx_a, o1); break;
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || single) return e;
-  const long long threads = (long long)n_seg * ((seglen + 7) / 8);
-  const int grid = (int)((threads + 255) / 256);
+  // merge passes: widths chunk, 2 chunk, ... (multiples of kMergeTile / 2)
+  const int tiles = (seglen + kMergeTile - 1) / kMergeTile;
   uint64_t* ki = key_a; int32_t* ii = idx_a;
   uint64_t* ko = key_b; int32_t* io = idx_b;
   for (int width = chunk; width < seglen; width *= 2) {
     const bool last = 2 * width >= seglen;
-    hipLaunchKernelGGL(k_merge_pass, dim3(grid), dim3(256), 0, s, ki, ii, ko,
-                       io, last ? out : nullptr, n_seg, seglen, width);
+    hipLaunchKernelGGL(k_merge_pass, dim3(n_seg * tiles), dim3(256), 0, s, ki,
+                       ii, ko, io, last ? out : nullptr, seglen, width, tiles);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     uint64_t* tk = ki; ki = ko; ko = tk;
@@ -599,9 +782,11 @@ hipError_t launch_restrict(const PlanDims& d, const int32_t* pi_k,
                      d.T, d.n_restrict_chunks);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_restrict_write, dim3(nbg * d.n_restrict_chunks),
-                     dim3(256), 0, s, pi_k, cum, L, d.N, d.S, d.T,
-                     d.n_restrict_chunks, (long long)d.list_len);
+  const int split = d.T - 1 < kRestrictSplit ? d.T - 1 : kRestrictSplit;
+  hipLaunchKernelGGL(k_restrict_write,
+                     dim3(nbg * d.n_restrict_chunks * split), dim3(256), 0, s,
+                     pi_k, cum, L, d.N, d.S, d.T, d.n_restrict_chunks, split,
+                     (long long)d.list_len);
   return hipGetLastError();
 }
 

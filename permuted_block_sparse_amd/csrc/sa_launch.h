@@ -13,6 +13,7 @@ constexpr int kPoolRows = 1024;      // rows per pooling workgroup
 constexpr int kScoreRows = 256;      // rows per scoring workgroup
 constexpr int kSortChunk = 4096;     // elements sorted in LDS by one workgroup
 constexpr int kRestrictChunk = 4096; // pi_K entries per restriction workgroup
+constexpr int kRestrictSplit = 8;    // restriction workgroups per chunk (t interleaved)
 constexpr int kMaxTiles = 2048;      // N / 64 at the largest supported N
 
 struct PlanDims {
@@ -30,9 +31,10 @@ hipError_t launch_pool_reduce(const PlanDims& d, const int64_t* part,
                               int64_t* pooled, hipStream_t s);
 hipError_t launch_key_score(const PlanDims& d, const uint16_t* k,
                             const int64_t* pooled, int64_t* vscore,
-                            int32_t* blocksum, hipStream_t s);
+                            int32_t* blocksum, float* kpart, hipStream_t s);
 hipError_t launch_segment_sum(const PlanDims& d, const int32_t* blocksum,
-                              int64_t* segsum, hipStream_t s);
+                              int64_t* segsum, const float* kpart,
+                              float* kmax2, hipStream_t s);
 hipError_t launch_contrast(const PlanDims& d, const uint16_t* k,
                            const int32_t* L, const int64_t* segsum,
                            int64_t* contrast, hipStream_t s);
@@ -93,6 +95,8 @@ struct AttnArgs {
   int wg_per_group;
   int n_groups;
   float c2;        // kappa * log2(e)
+  const float* kmax2;  // per (b, KV head): the largest |k_j|^2 (fp32)
+  int32_t* wg_flag;    // per workgroup: 1 = logits unbounded (kMaxRef runs it)
   int exact;       // 1: exact per-block max test instead of the stop points
   float exact_thr; // that test's threshold on the raw dot products (theta / kappa)
 };

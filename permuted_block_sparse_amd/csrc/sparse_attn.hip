@@ -24,7 +24,7 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 struct Layout {
   size_t pool_part, pooled, vscore, blocksum, segsum, contrast, u;
   size_t key_a, idx_a, key_b, idx_b;
-  size_t pi_k, L, pi_q, n_I, rcnt, rcum, qsum;
+  size_t pi_k, L, pi_q, n_I, rcnt, rcum, qsum, kpart, kmax2, wg_flag;
   size_t total;
 };
 
@@ -67,6 +67,14 @@ PlanDims dims_of(const sa_params* p) {
   return d;
 }
 
+// Workgroups of one attention launch: per (b, KV head, segment), the G
+// heads' query blocks of the segment, attention_blocks_per_wg() at a time.
+size_t attention_workgroups(const PlanDims& d) {
+  const int qblocks = d.G * (d.S / kBlock);
+  const int bpw = attention_blocks_per_wg();
+  return (size_t)d.B * d.Hkv * d.T * ((qblocks + bpw - 1) / bpw);
+}
+
 Layout layout_of(const PlanDims& d) {
   Layout L;
   size_t off = 0;
@@ -95,6 +103,9 @@ Layout layout_of(const PlanDims& d) {
   L.rcnt = take(nbg * d.n_restrict_chunks * d.T * sizeof(int32_t));
   L.rcum = take(nbg * d.n_restrict_chunks * d.T * sizeof(int32_t));
   L.qsum = take(nbh * (d.N / kBlock) * kHeadDim * sizeof(float));
+  L.kpart = take(nbg * d.n_score_wg * sizeof(float));
+  L.kmax2 = take(nbg * sizeof(float));
+  L.wg_flag = take(attention_workgroups(d) * sizeof(int32_t));
   L.total = off;
   return L;
 }
@@ -255,10 +266,13 @@ int sparse_attn_plan(const sa_params* p, const void* q, const void* k,
   if (e == hipSuccess)
     e = launch_key_score(d, kb, pl->at<int64_t>(lay.pooled),
                          pl->at<int64_t>(lay.vscore),
-                         pl->at<int32_t>(lay.blocksum), stream);
+                         pl->at<int32_t>(lay.blocksum),
+                         pl->at<float>(lay.kpart), stream);
   if (e == hipSuccess)
     e = launch_segment_sum(d, pl->at<int32_t>(lay.blocksum),
-                           pl->at<int64_t>(lay.segsum), stream);
+                           pl->at<int64_t>(lay.segsum),
+                           pl->at<float>(lay.kpart), pl->at<float>(lay.kmax2),
+                           stream);
   if (e == hipSuccess) {
     const size_t nbg = (size_t)d.B * d.Hkv;
     if (p->flags & SA_NO_KVPERM)
@@ -322,6 +336,8 @@ int sparse_attn_prefill(const sa_plan* plan, const void* q, const void* k,
                                   std::sqrt((double)kHeadDim))
                         : 0.f;
   a.c2 = (float)(1.4426950408889634074 / std::sqrt((double)kHeadDim));
+  a.kmax2 = plan->at<float>(plan->lay.kmax2);
+  a.wg_flag = plan->at<int32_t>(plan->lay.wg_flag);
   if (!a.exact && !plan->stops_valid) {
     const int rc = run_stop_scan(plan, stream);
     if (rc != SA_OK) return rc;

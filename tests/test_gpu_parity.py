@@ -8,8 +8,8 @@ import numpy as np
 import pytest
 
 import oracle as O
-from synthetic import (StripeSpec, get_config, make_stripe_inputs,
-                       round_to_bf16_bits)
+from synthetic import (StripeSpec, bf16_bits_to_float32, get_config,
+                       make_stripe_inputs, round_to_bf16_bits)
 from tests.gpu_helpers import (assert_outputs_close, assert_plan_equal,
                                run_gpu, say, stop_mismatches)
 
@@ -52,6 +52,11 @@ CASES = [
      O.SA_SEGMENT_KV),
     ("s4096_merge_sort_n8192", _spec(1, 2, 1, 8192, 30, n_vert=64,
                                      window=128), 4096, (0.02,), 0),
+    # pi_K: three sort chunks, so the merge passes meet a pair with no second
+    # run and then a short second run; pi_Q: segments of 6144 = 4096 + 2048
+    # (a padded chunk and a merge pass over the segment)
+    ("ragged_merges_n12288_s6144", _spec(1, 2, 1, 12288, 40, n_vert=64,
+                                         window=128), 6144, (0.05,), 0),
     # 4 query heads x 64 blocks per segment: the stop scan splits a segment's
     # 256 blocks over two workgroups and its 64 local blocks over two chunks
     ("g4_s4096_two_scan_chunks", _spec(1, 4, 1, 8192, 39, n_vert=64,
@@ -83,6 +88,67 @@ def test_parity_small(name, spec, S, taus, flags):
         err, mse, nties, g, pl, n_orc = _check_case(q, k, v, S, tau, flags)
         say(f"   max_abs={err:.3g} mse={mse:.3g} ties={nties} "
             f"mean_n_I={g['n_I'].mean():.2f}")
+
+
+C2 = 1.4426950408889634 / np.sqrt(128.0)  # kappa log2(e), d = 128
+
+
+def _reference_margins(qf, kf, S):
+    """Per (head, row): |q| max_j |k_j| kappa log2(e) (with the kernel's 2^-10
+    margin) minus the row's largest logit over its segment's first 64 keys,
+    and the rise of the row's largest logit over all visible keys above that
+    first one (log2 units, float64)."""
+    B, Hq, N, d = qf.shape
+    G = Hq // kf.shape[1]
+    margin = np.zeros((Hq, N))
+    rise = np.zeros((Hq, N))
+    for h in range(Hq):
+        K, Q = kf[0, h // G], qf[0, h]
+        L = (Q @ K.T) * C2
+        kmax = np.sqrt((K * K).sum(-1).max())
+        qn = np.sqrt((Q * Q).sum(-1))
+        for i in range(N):
+            s0 = (i // S) * S
+            m0 = L[i, s0:min(s0 + 64, i + 1)].max()
+            margin[h, i] = qn[i] * kmax * C2 * (1 + 1 / 1024) - m0
+            rise[h, i] = L[i, :i + 1].max() - m0
+    return margin, rise
+
+
+def test_reference_paths():
+    """Both references of the online softmax against the oracle. Head 0:
+    four late keys pulled towards the mean query, so that some rows' logits
+    rise more than 8 log2 units above the first local tile's maximum (the
+    rescale of the bounded path runs) while every row stays provably
+    bounded. Head 1: queries and keys times 4 (exact in bf16), so that its
+    rows are not provably bounded and its workgroups run with the row
+    maximum of every tile. One query block per workgroup head (G = 1), so
+    both kinds of workgroup run in the same launch."""
+    spec = _spec(1, 2, 2, 1024, 41)
+    S = 256
+    q, k, v = make_stripe_inputs(spec)
+    qf = bf16_bits_to_float32(q).astype(np.float64)
+    kf = bf16_bits_to_float32(k).astype(np.float64)
+    qbar = qf[0, 0].mean(0)
+    qbar /= np.linalg.norm(qbar)
+    for j in (200, 500, 777, 900):
+        kf[0, 0, j] += 10.0 * qbar * np.sqrt(128.0) / 4
+    qf[0, 1] *= 4.0
+    kf[0, 1] *= 4.0
+    q = round_to_bf16_bits(qf.astype(np.float32))
+    k = round_to_bf16_bits(kf.astype(np.float32))
+    qf = bf16_bits_to_float32(q).astype(np.float64)
+    kf = bf16_bits_to_float32(k).astype(np.float64)
+    margin, rise = _reference_margins(qf, kf, S)
+    assert margin[0].max() < 120.0 and (rise[0] > 8.0).sum() >= 10
+    assert margin[1].min() > 120.0
+    for tau in (0.0, 0.05):
+        say(f"[reference paths] tau={tau}")
+        err, mse, nties, g, pl, n_orc = _check_case(q, k, v, S, tau, 0)
+        say(f"   max_abs={err:.3g} mse={mse:.3g} ties={nties}")
+    od, ld = O.dense_causal(q, k, v)
+    g = run_gpu(q, k, v, S, 0.0)
+    assert_outputs_close(g["o"], od, g["lse"], ld)
 
 
 def test_tau0_is_dense_and_kv_order_invariant():

@@ -155,13 +155,17 @@ int sparse_attn_plan(const sa_params* p, const void* q, const void* k,
  *     to the tile (online softmax);
  *   - each output row is written to its original position in O.
  * kappa = 1/sqrt(head_dim). q, k must be the tensors the plan was built
- * from (not checked). o: device [batch, heads_q, seq_len, 128] bfloat16,
+ * from (not checked: the stop points, and the plan's bound on the key norms
+ * that keeps the softmax's exponentials finite, come from them). o: device
+ * [batch, heads_q, seq_len, 128] bfloat16,
  * fully overwritten. lse (may be NULL): device [batch, heads_q, seq_len]
  * float32, natural-log log-sum-exp of kappa q.k over each row's key set.
  * The stop points come from the plan (export N_I). After a setter below or
  * sparse_attn_plan_set_kv_order changed what they depend on, this call
  * first rescans them on `stream` (one extra launch), then launches the
- * attention. A plan must not be used by two calls at once.
+ * attention: two launches of one kernel, the second running only the
+ * workgroups whose logits are too large to be provably bounded. A plan must
+ * not be used by two calls at once.
  */
 int sparse_attn_prefill(const sa_plan* plan, const void* q, const void* k,
                         const void* v, void* o, float* lse,

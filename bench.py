@@ -164,16 +164,15 @@ def main():
     pl = pbs.plan(tq, tk, S, tau)
     attn_med = float(np.median(attn_launch_ms))
     n_I = pl.n_I()
-    pi_q = pl.pi_q()
     log(f"[bench] plan {plan_ms:.3f} ms, prefill {attn_med:.3f} ms")
 
     T = N // S
     nb = N // 64
-    # visited local blocks: c with some row of the block at or after the
-    # block's first key
-    blk_max = pi_q.reshape(B, Hq, nb, 64).max(axis=3)
-    seg_of_blk = (np.arange(nb) * 64) // S
-    diag_tiles = int(((blk_max - seg_of_blk * S) // 64 + 1).sum())
+    # visited local tiles: the local pass takes every segment's rows in
+    # their own order, block i of a segment against its key blocks 0 .. i
+    # (the last one masked), so bps (bps + 1) / 2 tiles per segment and head
+    bps = S // 64
+    diag_tiles = B * Hq * T * bps * (bps + 1) // 2
     sparse_tiles = int(n_I.sum())
     visited = diag_tiles + sparse_tiles
     flop_launch = visited * TILE_FLOP
@@ -227,7 +226,8 @@ def main():
         "bound": "mfma", "achieved": round(achieved, 2),
         "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
         "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
-        "traffic": traffic, "kernel": "k_attn_fwd<kFastRef>",
+        "traffic": traffic,
+        "kernel": "k_attn_fwd (kLocal + kFastRef + kMaxRef launches of a prefill)",
         "flop_per_launch": flop_launch,
         "avg_launch_ms": round(attn_mean, 4)}
 

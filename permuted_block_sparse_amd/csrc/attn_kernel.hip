@@ -7,24 +7,36 @@
 // the loop itself carries no decision. Outputs go back to their original
 // rows (no tensor is moved).
 //
+// Two passes of one kernel per prefill. The local pass computes each query
+// block's dense local window in the rows' own order: block i of segment t
+// (rows t S + 64 i ..) against key blocks 0 .. i of the segment, only the
+// last one masked. It writes the normalised result to O and the
+// log2-sum-exp of each row to a scratch array. The sparse pass takes the
+// blocks of pi_Q: each row resumes from that state (reference = the local
+// log2-sum-exp, l = 1, accumulator = the local output) and continues over
+// the first n_I tiles of L_t, then overwrites its row of O. The softmax
+// does not depend on the order in which a row's keys are visited. A block
+// of pi_Q holds rows from all over its segment, so in that order its local
+// window would need every key block of the segment with about half of the
+// pairs masked; in the rows' own order it needs about half as many tiles.
+//
 // Work decomposition (gfx950, wave64, 2 waves per SIMD): one workgroup = 8
 // waves = 4 query blocks of 64 rows that share the same KV head g and
-// segment t, hence the same key tiles (dense local window = segment t's
-// keys; sparse tiles = L_t). Wave w holds rows 32 (w / 4) .. + 31 of query
-// block w % 4; both halves of a block sit on the same SIMD. K and V tiles
-// are gathered into LDS once per workgroup and read by all 8 waves; the
-// workgroup runs to the largest stop point of its blocks, and a wave whose
-// block has stopped only helps with the gathers.
+// segment t, hence the same key tiles (local pass: segment t's keys; sparse
+// pass: L_t). Wave w holds rows 32 (w / 4) .. + 31 of query block w % 4;
+// both halves of a block sit on the same SIMD. K and V tiles are gathered
+// into LDS once per workgroup and read by all 8 waves; the workgroup runs to
+// the largest step count of its blocks, and a wave whose block is done only
+// helps with the gathers.
 //
-// Pipeline: the local blocks and then the sparse tiles form one sequence of
-// steps, and each wave overlaps its matrix and vector work within a step.
+// Pipeline: each wave overlaps its matrix and vector work within a step.
 // LDS holds three K/V tile buffers and each wave two sets of logit
-// registers. Step s: row maximum (and the rare rescale) of tile s's
-// logits; the QK MFMAs of tile s + 1 interleaved with the exponentials of
+// registers. Step s: the reference of tile s (see the online softmax
+// below); the QK MFMAs of tile s + 1 interleaved with the exponentials of
 // tile s; the PV MFMAs of tile s; tile s + 2's rows (loaded into registers
 // during step s - 1) into the buffer that held tile s - 1; the loads of
 // tile s + 3's rows and of step s + 4's indices. One barrier per step. A
-// wave whose block has stopped (or that holds no rows) runs the same
+// wave whose block is done (or that holds no rows) runs the same
 // instructions as a no-op, so no branch splits the MFMA and VALU work.
 //
 // Exact per-block max mode (the BSFA page's test, instead of the stop): every
@@ -40,12 +52,14 @@
 //   online softmax: one query row per lane pair (lane, lane ^ 32), fp32,
 //                   exp2 domain; o = acc / l holds for any reference, so
 //                   the reference is raised only when p values could pass
-//                   2^8. Rows provably bounded (the logit bound |q| max |k|
-//                   kappa log2(e) within 120 of the first tile's maximum,
-//                   so no p can overflow) skip the per-tile row maximum
-//                   and test the lane's tile sum instead (a sum above 2^8
-//                   divides the row by its largest p); other workgroups take
-//                   the row maximum of every tile (a second launch);
+//                   2^8. The local pass takes the row maximum of every
+//                   tile (rescaling lazily). In the sparse pass, rows that
+//                   are provably bounded (the logit bound |q| max |k| kappa
+//                   log2(e) within 120 of the local log2-sum-exp, so no p
+//                   can overflow) skip the per-tile row maximum and test the
+//                   lane's tile sum instead (a sum above 2^8 divides the row
+//                   by its largest p); workgroups with other rows take the
+//                   row maximum of every tile (a further launch);
 //   O^T += V^T P^T: V^T A operands via ds_read_tr16_b64 transposed reads,
 //                   P^T B operands straight from the S registers.
 //
@@ -356,20 +370,24 @@ __device__ __forceinline__ float qk_exp(const char* Kt, const bf16x8 (&qr)[8],
 // s_waitcnt lgkmcnt(0) (gfx9 encoding; vmcnt and expcnt left unlimited)
 __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
-// Three instances. kMaxRef and kFastRef: each block attends its dense local
-// window and the first n_I tiles of L_t, n_I given (the early stop's stop
-// points or a budget). kFastRef raises the online softmax's reference only
-// when p values grow past 2^8; it runs the workgroups whose logits are
-// provably bounded, exits from the others and flags them for the kMaxRef
-// launch that follows, which takes the row maximum of every tile and skips
-// the unflagged workgroups. kExactMax: the exact per-block max test decides
-// every tile of L_t in the loop.
-enum : int { kMaxRef = 0, kFastRef = 1, kExactMax = 2 };
+// Four instances. kLocal: the local pass (every block's dense local window,
+// rows in their own order). kMaxRef and kFastRef: the sparse pass over the
+// first n_I tiles of L_t, n_I given (the early stop's stop points or a
+// budget). kFastRef raises the online softmax's reference only when p
+// values grow past 2^8; it runs the workgroups whose logits are provably
+// bounded, exits from the others and flags them for the kMaxRef launch that
+// follows, which takes the row maximum of every tile and skips the
+// unflagged workgroups. kExactMax: the sparse pass with the exact per-block
+// max test deciding every tile of L_t in the loop. Workgroups of the sparse
+// instances with no tile to visit exit at once: the local pass's output is
+// final for their rows.
+enum : int { kMaxRef = 0, kFastRef = 1, kExactMax = 2, kLocal = 3 };
 
 template <int kMode>
 __global__ __launch_bounds__(kThreads, 1) void k_attn_fwd(AttnArgs a) {
   constexpr bool kExact = kMode == kExactMax;
   constexpr bool kFast = kMode == kFastRef;
+  constexpr bool kLoc = kMode == kLocal;
   if (kMode == kMaxRef && a.wg_flag[blockIdx.x] == 0) return;  // done
   // three K/V tile buffers of 2 x 16 KB
   __shared__ __attribute__((aligned(1024))) char tiles[3][2 * kTileBytes];
@@ -395,6 +413,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_fwd(AttnArgs a) {
     grp = p / a.wg_per_group;
     chunk = p % a.wg_per_group;
   }
+  // local pass: the blocks nearest the segment's end (the most key tiles)
+  // first
+  if (kLoc) chunk = a.wg_per_group - 1 - chunk;
   const int BH = a.B * a.Hkv;
   const int t = a.T - 1 - grp / BH;
   const int bg = grp % BH, b = bg / a.Hkv, g = bg % a.Hkv;
@@ -402,11 +423,16 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_fwd(AttnArgs a) {
   const int e = chunk * 4 + qsub;
   const bool valid = e < a.G * bps;
   const int h = g * a.G + (valid ? e % a.G : 0);
-  const int I = t * bps + (valid ? e / a.G : 0);
+  const int Ib = valid ? e / a.G : 0;  // block index within the segment
+  const int I = t * bps + Ib;
+  const int seg0 = t * a.S;
 
   const size_t bh = (size_t)b * a.Hq + h;
   const int32_t* pq = a.pi_q + bh * a.N + (size_t)I * kBlock;
-  const int iq = min(max(pq[32 * half + lq], 0), a.N - 1);  // my row
+  // my row: the local pass takes the segment's rows in their own order,
+  // the sparse passes the rows of block I of pi_Q
+  const int iq = kLoc ? seg0 + Ib * kBlock + 32 * half + lq
+                      : min(max(pq[32 * half + lq], 0), a.N - 1);
   const uint16_t* qh = a.q + bh * a.N * kHeadDim;
   const uint16_t* kbase = a.k + (size_t)bg * a.N * kHeadDim;
   const uint16_t* vbase = a.v + (size_t)bg * a.N * kHeadDim;
@@ -418,18 +444,38 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_fwd(AttnArgs a) {
     qr[s] = *reinterpret_cast<const bf16x8*>(qh + (size_t)iq * kHeadDim +
                                              16 * s + 8 * lh);
 
+  // The local pass starts from nothing; the sparse passes continue the
+  // online softmax of the local pass, whose normalised output (bf16, in O)
+  // and log2-sum-exp are the state o = acc / l, l = 1 for reference m =
+  // log2-sum-exp.
   f32x16 oacc[4];
-#pragma unroll
-  for (int db = 0; db < 4; ++db) oacc[db] = f32x16{};
   float m = -INFINITY, l = 0.f;
-  f32x16 sacc[2];
+  if (kLoc) {
+#pragma unroll
+    for (int db = 0; db < 4; ++db) oacc[db] = f32x16{};
+  } else {
+    const uint16_t* orow0 = a.o + (bh * a.N + iq) * kHeadDim;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const uint2 w = *reinterpret_cast<const uint2*>(
+            orow0 + db * 32 + 8 * g4 + 4 * lh);
+        oacc[db][4 * g4 + 0] = __uint_as_float(w.x << 16);
+        oacc[db][4 * g4 + 1] = __uint_as_float(w.x & 0xffff0000u);
+        oacc[db][4 * g4 + 2] = __uint_as_float(w.y << 16);
+        oacc[db][4 * g4 + 3] = __uint_as_float(w.y & 0xffff0000u);
+      }
+    m = a.lse2[bh * a.N + iq];
+    l = 1.f;
+  }
 
-  // ---- the step sequence: ndiag local blocks, then the tiles of L_t up to
-  // the largest stop point of the workgroup's blocks.
-  const int seg0 = t * a.S;
+  // ---- the step sequence: the local pass's ndiag key blocks of the
+  // segment, or the sparse passes' tiles of L_t up to the largest stop point
+  // of the workgroup's blocks.
   const int ntl = t * bps;  // tiles of L_t
   int32_t* nI_ptr = a.n_I + bh * (a.N / kBlock) + I;
-  const int nI = !valid ? 0 : kExact ? ntl : min(max(*nI_ptr, 0), ntl);
+  const int nI = (!valid || kLoc) ? 0 : kExact ? ntl : min(max(*nI_ptr, 0), ntl);
   const int myrow = wave_max_int(iq);
   if (lane == 0) {
     wave_maxrow[wave] = valid ? myrow : -1;
@@ -442,8 +488,19 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_fwd(AttnArgs a) {
     wgmax = max(wgmax, wave_maxrow[w]);
     ntiles = max(ntiles, wave_ntiles[w]);
   }
-  const int ndiag = min(max((wgmax - seg0) / kBlock + 1, 1), bps);
+  // sparse passes: no local step (the local pass covered those blocks);
+  // a.local_steps is 0, read at run time as a value in [0, 1]: with a
+  // literal 0 (or an unbounded value) the compiler schedules the loop with
+  // more registers and spills
+  const int ndiag = kLoc ? min(max((wgmax - seg0) / kBlock + 1, 1), bps)
+                         : (a.local_steps != 0 ? 1 : 0);
   const int nsteps = ndiag + ntiles;
+  if (!kLoc && ntiles == 0) {
+    // no sparse tile: the local pass's output and lse are final
+    if (kFast && tid == 0) a.wg_flag[blockIdx.x] = 0;
+    if (kExact && valid && lane == 0 && half == 0) *nI_ptr = 0;
+    return;
+  }
   const int32_t* Lt =
       a.L + (size_t)bg * a.list_len + (size_t)a.S * t * (t - 1) / 2;
 
@@ -494,12 +551,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_fwd(AttnArgs a) {
         cur[kb][r] = off > lim ? -INFINITY : cur[kb][r];
       }
   };
-  // Tau / budget mode: the online softmax's first reference is the row
-  // maximum of tile 0, the segment's first local block, where every row sees
-  // at least one key (the segment's first).
-  if (!kExact) {
-    mask_local(0, sa);
-    m = row_max(sa, a.c2);
+  float my_max = 0.f;  // exact mode: this half's maximum of the current tile
+  if (kExact) {
+    // tile 0's maxima for the exact test of step 0
+    my_max = wave_max(lane_max(sa));
+    if (lane == 0) tile_max[0][wave] = __float_as_uint(my_max);
+    __syncthreads();
   }
   if (kFast) {
     // The logits of a row are bounded by |q| max_j |k_j| (Cauchy-Schwarz);
@@ -525,11 +582,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_fwd(AttnArgs a) {
     }
   }
   int n_visit = 0;     // exact mode: tiles attended
-  float my_max = 0.f;  // exact mode: this half's maximum of the current tile
   auto body = [&](int s, f32x16 (&cur)[2], f32x16 (&nxs)[2]) {
-    const bool local = s < ndiag;
-    if (local) mask_local(s, cur);
-    bool act = valid && (local || (s - ndiag) < nI);
+    const bool local = s < ndiag;  // every step of the local pass
+    // the local pass: block Ib sees key blocks 0 .. Ib, the last one masked
+    if (kLoc && s == Ib) mask_local(s, cur);
+    bool act = valid && (kLoc ? s <= Ib : (s - ndiag) < nI);
     if (kExact && !local) {
       // exact max test of tile s: both halves take max(own, other) of the
       // maxima posted with the tile's logits, before the last barrier
@@ -601,8 +658,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_fwd(AttnArgs a) {
       for (int j = 0; j < 4; ++j) v4[j] = (__bf16)(oacc[db][4 * g4 + j] * inv);
       *reinterpret_cast<uint2*>(orow + d0) = __builtin_bit_cast(uint2, v4);
     }
-  if (a.lse != nullptr && lh == 0)
-    a.lse[bh * a.N + iq] = (m + log2f(l)) * ln2;
+  const float lse2v = m + log2f(l);
+  if (kLoc && lh == 0) a.lse2[bh * a.N + iq] = lse2v;
+  if (a.lse != nullptr && lh == 0) a.lse[bh * a.N + iq] = lse2v * ln2;
   if (kExact && lane == 0 && half == 0) *nI_ptr = n_visit;
 }
 
@@ -610,6 +668,10 @@ int attention_blocks_per_wg() { return 4; }
 
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
   const int total = a.n_groups * a.wg_per_group;
+  // the dense local windows in the rows' own order
+  hipLaunchKernelGGL(k_attn_fwd<kLocal>, dim3(total), dim3(kThreads), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.local_only) return e;
   if (a.exact) {
     hipLaunchKernelGGL(k_attn_fwd<kExactMax>, dim3(total), dim3(kThreads), 0,
                        s, a);
@@ -618,7 +680,7 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
   // the bounded workgroups, then (flagged by the first launch) the others
   hipLaunchKernelGGL(k_attn_fwd<kFastRef>, dim3(total), dim3(kThreads), 0, s,
                      a);
-  hipError_t e = hipGetLastError();
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_attn_fwd<kMaxRef>, dim3(total), dim3(kThreads), 0, s,
                      a);

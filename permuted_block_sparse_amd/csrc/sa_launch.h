@@ -97,6 +97,9 @@ struct AttnArgs {
   float c2;        // kappa * log2(e)
   const float* kmax2;  // per (b, KV head): the largest |k_j|^2 (fp32)
   int32_t* wg_flag;    // per workgroup: 1 = logits unbounded (kMaxRef runs it)
+  float* lse2;         // per row: the local pass's log2-sum-exp (exp2 domain)
+  int local_only;      // 1: the local pass only (no sparse tile visited)
+  int local_steps;     // local steps of the sparse passes: always 0
   int exact;       // 1: exact per-block max test instead of the stop points
   float exact_thr; // that test's threshold on the raw dot products (theta / kappa)
 };

@@ -24,7 +24,7 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 struct Layout {
   size_t pool_part, pooled, vscore, blocksum, segsum, contrast, u;
   size_t key_a, idx_a, key_b, idx_b;
-  size_t pi_k, L, pi_q, n_I, rcnt, rcum, qsum, kpart, kmax2, wg_flag;
+  size_t pi_k, L, pi_q, n_I, rcnt, rcum, qsum, kpart, kmax2, wg_flag, lse2;
   size_t total;
 };
 
@@ -106,6 +106,7 @@ Layout layout_of(const PlanDims& d) {
   L.kpart = take(nbg * d.n_score_wg * sizeof(float));
   L.kmax2 = take(nbg * sizeof(float));
   L.wg_flag = take(attention_workgroups(d) * sizeof(int32_t));
+  L.lse2 = take(nbh * d.N * sizeof(float));
   L.total = off;
   return L;
 }
@@ -338,6 +339,9 @@ int sparse_attn_prefill(const sa_plan* plan, const void* q, const void* k,
   a.c2 = (float)(1.4426950408889634074 / std::sqrt((double)kHeadDim));
   a.kmax2 = plan->at<float>(plan->lay.kmax2);
   a.wg_flag = plan->at<int32_t>(plan->lay.wg_flag);
+  a.lse2 = plan->at<float>(plan->lay.lse2);
+  a.local_only = (plan->p.flags & SA_LOCAL_ONLY) ? 1 : 0;
+  a.local_steps = 0;
   if (!a.exact && !plan->stops_valid) {
     const int rc = run_stop_scan(plan, stream);
     if (rc != SA_OK) return rc;

@@ -420,8 +420,13 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_fwd(AttnArgs a) {
   const int t = a.T - 1 - grp / BH;
   const int bg = grp % BH, b = bg / a.Hkv, g = bg % a.Hkv;
   const int bps = a.S / kBlock;  // query blocks per segment and head
-  const int e = chunk * 4 + qsub;
-  const bool valid = e < a.G * bps;
+  // query block e of the group: in order (local pass), or the sparse pass's
+  // order by stop point
+  const int ewg = chunk * 4 + qsub;
+  const bool valid = ewg < a.G * bps;
+  const int e = (!kLoc && a.border != nullptr && valid)
+                    ? a.border[((long long)bg * a.T + t) * (a.G * bps) + ewg]
+                    : ewg;
   const int h = g * a.G + (valid ? e % a.G : 0);
   const int Ib = valid ? e / a.G : 0;  // block index within the segment
   const int I = t * bps + Ib;

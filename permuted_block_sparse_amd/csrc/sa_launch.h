@@ -80,6 +80,12 @@ struct StopArgs {
 };
 hipError_t launch_stop_scan(const StopArgs& a, hipStream_t s);
 
+// Per (b, KV head, segment): its G (S / 64) query blocks by stop point
+// descending, for groups of at most kOrderMax blocks.
+constexpr int kOrderMax = 1024;
+hipError_t launch_block_order(const PlanDims& d, const int32_t* n_I,
+                              int32_t* order, hipStream_t s);
+
 // ---- attention
 struct AttnArgs {
   const uint16_t* q;
@@ -100,6 +106,7 @@ struct AttnArgs {
   float* lse2;         // per row: the local pass's log2-sum-exp (exp2 domain)
   int local_only;      // 1: the local pass only (no sparse tile visited)
   int local_steps;     // local steps of the sparse passes: always 0
+  const int32_t* border;  // per group: blocks by stop point (null: in order)
   int exact;       // 1: exact per-block max test instead of the stop points
   float exact_thr; // that test's threshold on the raw dot products (theta / kappa)
 };

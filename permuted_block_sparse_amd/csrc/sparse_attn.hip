@@ -24,7 +24,8 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 struct Layout {
   size_t pool_part, pooled, vscore, blocksum, segsum, contrast, u;
   size_t key_a, idx_a, key_b, idx_b;
-  size_t pi_k, L, pi_q, n_I, rcnt, rcum, qsum, kpart, kmax2, wg_flag, lse2;
+  size_t pi_k, L, pi_q, n_I, rcnt, rcum, qsum, kpart, kmax2, wg_flag, lse2,
+      border;
   size_t total;
 };
 
@@ -107,6 +108,7 @@ Layout layout_of(const PlanDims& d) {
   L.kmax2 = take(nbg * sizeof(float));
   L.wg_flag = take(attention_workgroups(d) * sizeof(int32_t));
   L.lse2 = take(nbh * d.N * sizeof(float));
+  L.border = take(nbh * (d.N / kBlock) * sizeof(int32_t));
   L.total = off;
   return L;
 }
@@ -190,6 +192,11 @@ bool exact_mode(const sa_plan* pl) {
   return !std::isnan(pl->max_theta) && !(pl->p.flags & SA_LOCAL_ONLY);
 }
 
+// The sparse pass takes each group's blocks by stop point (small groups).
+bool block_order_used(const PlanDims& d) {
+  return d.G * (d.S / kBlock) <= kOrderMax;
+}
+
 // n_I of the plan's current settings: the tau stop scanned from pooled
 // means, or a fixed count (dense local window only: 0; fixed budget K:
 // min(K, t S / 64); tau = 0 or SA_NO_EARLYSTOP: every tile of L_t).
@@ -219,7 +226,9 @@ int run_stop_scan(const sa_plan* pl, hipStream_t s) {
     a.fixed = std::numeric_limits<int>::max();
   else
     a.fixed = -1;
-  const hipError_t e = launch_stop_scan(a, s);
+  hipError_t e = launch_stop_scan(a, s);
+  if (e == hipSuccess && block_order_used(d))
+    e = launch_block_order(d, a.n_I, pl->at<int32_t>(pl->lay.border), s);
   if (e != hipSuccess) return SA_ERR_HIP;
   pl->stops_valid = true;
   return SA_OK;
@@ -342,6 +351,9 @@ int sparse_attn_prefill(const sa_plan* plan, const void* q, const void* k,
   a.lse2 = plan->at<float>(plan->lay.lse2);
   a.local_only = (plan->p.flags & SA_LOCAL_ONLY) ? 1 : 0;
   a.local_steps = 0;
+  a.border = (!a.exact && block_order_used(d))
+                 ? plan->at<int32_t>(plan->lay.border)
+                 : nullptr;
   if (!a.exact && !plan->stops_valid) {
     const int rc = run_stop_scan(plan, stream);
     if (rc != SA_OK) return rc;

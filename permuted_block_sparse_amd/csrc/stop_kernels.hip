@@ -241,6 +241,42 @@ __global__ __launch_bounds__(kScanThreads) void k_stop_scan(StopArgs a) {
   if (valid && dq == 0) *nout = n;
 }
 
+// Order of the query blocks of one (b, KV head, segment) group for the
+// sparse attention pass: stop point descending, block index ascending on
+// ties. A workgroup takes 4 consecutive blocks of this order, so its blocks
+// stop at nearly the same step (a workgroup runs to its largest stop
+// point). One workgroup per group; rank by counting, P <= kOrderMax.
+__global__ __launch_bounds__(256) void k_block_order(const int32_t* __restrict__ n_I,
+                                                     int32_t* __restrict__ order,
+                                                     int Hq, int Hkv, int N,
+                                                     int S, int T, int G) {
+  __shared__ int nv[kOrderMax];
+  const int grp = blockIdx.x;  // bg * T + t
+  const int bg = grp / T, t = grp % T, b = bg / Hkv, g = bg % Hkv;
+  const int bps = S / kBlock, P = G * bps;
+  for (int e = threadIdx.x; e < P; e += 256) {
+    const int h = g * G + e % G, I = t * bps + e / G;
+    nv[e] = n_I[((long long)b * Hq + h) * (N / kBlock) + I];
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < P; e += 256) {
+    const int v = nv[e];
+    int r = 0;
+    for (int j = 0; j < P; ++j) {
+      const int w = nv[j];
+      r += (w > v || (w == v && j < e)) ? 1 : 0;
+    }
+    order[(long long)grp * P + r] = e;
+  }
+}
+
+hipError_t launch_block_order(const PlanDims& d, const int32_t* n_I,
+                              int32_t* order, hipStream_t s) {
+  hipLaunchKernelGGL(k_block_order, dim3(d.B * d.Hkv * d.T), dim3(256), 0, s,
+                     n_I, order, d.Hq, d.Hkv, d.N, d.S, d.T, d.G);
+  return hipGetLastError();
+}
+
 hipError_t launch_block_qsum(const PlanDims& d, const uint16_t* q,
                              const int32_t* pi_q, float* qsum, hipStream_t s) {
   const long long nblk = (long long)d.B * d.Hq * (d.N / kBlock);

@@ -57,6 +57,10 @@ CASES = [
     # (a padded chunk and a merge pass over the segment)
     ("ragged_merges_n12288_s6144", _spec(1, 2, 1, 12288, 40, n_vert=64,
                                          window=128), 6144, (0.05,), 0),
+    # 64 query heads per KV head: 2048 query blocks per (KV head, segment),
+    # more than the sparse pass orders by stop point (it takes them in order)
+    ("g64_blocks_in_order_n4096", _spec(1, 64, 1, 4096, 42), 2048, (0.05,),
+     0),
     # 4 query heads x 64 blocks per segment: the stop scan splits a segment's
     # 256 blocks over two workgroups and its 64 local blocks over two chunks
     ("g4_s4096_two_scan_chunks", _spec(1, 4, 1, 8192, 39, n_vert=64,

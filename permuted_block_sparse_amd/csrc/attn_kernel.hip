@@ -287,26 +287,6 @@ __device__ __forceinline__ float row_rescale(const f32x16 (&sacc)[2],
   return !active ? INFINITY : m == -INFINITY ? 0.f : m;
 }
 
-// Row maximum of a tile's logits (both lanes of a row pair), times c2.
-__device__ __forceinline__ float row_max(const f32x16 (&sacc)[2], float c2) {
-  return max_xor32(lane_max(sacc)) * c2;
-}
-
-// p = exp2(s c2 - muse) in place; returns the lane's sum.
-__device__ __forceinline__ float tile_exp(f32x16 (&sacc)[2], float c2,
-                                          float muse) {
-  float rs = 0.f;
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float p = __builtin_amdgcn_exp2f(sacc[kb][r] * c2 - muse);
-      sacc[kb][r] = p;
-      rs += p;
-    }
-  return rs;
-}
-
 __device__ __forceinline__ void pv_tile(const char* Vt, const f32x16 (&sacc)[2],
                                         f32x16 (&oacc)[4], const ReadAddr& ra) {
 #pragma unroll

@@ -171,6 +171,24 @@ int sparse_attn_prefill(const sa_plan* plan, const void* q, const void* k,
                         const void* v, void* o, float* lse,
                         hipStream_t stream);
 
+/*
+ * sparse_attn_plan followed by sparse_attn_prefill in one call, with the
+ * same results: the prefill's dense local windows depend on q, k, v alone,
+ * so they run on side_stream (after the work already enqueued on `stream`)
+ * while the planner runs on `stream`; the rest of the attention waits on
+ * `stream` for both. Arguments as for the two calls; side_stream must
+ * belong to the same device and may equal `stream` (then everything runs
+ * in order on `stream`). On return the work is enqueued on both streams
+ * and `stream` is ordered after all of it; o, lse and the workspace must
+ * stay allocated until it completes. On success *out receives the plan
+ * (setters, exports and further prefills as from sparse_attn_plan; free
+ * with sparse_attn_plan_destroy).
+ */
+int sparse_attn_forward(const sa_params* p, const void* q, const void* k,
+                        const void* v, void* o, float* lse, void* workspace,
+                        size_t workspace_bytes, hipStream_t stream,
+                        hipStream_t side_stream, sa_plan** out);
+
 /* Change the threshold of an existing plan (the index arrays do not depend
  * on tau). Returns SA_ERR_INVALID_ARG for tau < 0 or NaN. */
 int sparse_attn_plan_set_tau(sa_plan* plan, double tau);

@@ -23,7 +23,8 @@ from . import _lib
 from ._lib import (SA_NO_QPERM, SA_NO_KVPERM, SA_NO_EARLYSTOP,
                    SA_LOCAL_ONLY, SA_SEGMENT_KV, SparseAttnError)
 
-__all__ = ["plan", "prefill", "SparsePlan", "SA_NO_QPERM", "SA_NO_KVPERM",
+__all__ = ["plan", "prefill", "forward", "SparsePlan", "SA_NO_QPERM",
+           "SA_NO_KVPERM",
            "SA_NO_EARLYSTOP", "SA_LOCAL_ONLY", "SA_SEGMENT_KV",
            "SparseAttnError",
            "workspace_bytes"]
@@ -67,7 +68,8 @@ def workspace_bytes(batch, heads_q, heads_kv, seq_len, segment, head_dim=128,
 class SparsePlan:
     """A plan (index arrays in a device workspace owned by this object)."""
 
-    def __init__(self, q, k, segment, tau, block=64, flags=0, stream=None):
+    def __init__(self, q, k, segment, tau, block=64, flags=0, stream=None,
+                 _launch=None):
         lib = _lib.load()
         _check_tensor(q, "q")
         _check_tensor(k, "k")
@@ -86,12 +88,15 @@ class SparsePlan:
         self.shape = tuple(q.shape)
         self.heads_kv = k.shape[1]
         self._inputs = (q, k)   # the plan keeps device pointers to both
-        st = lib.sparse_attn_plan(
-            ctypes.byref(self.params), ctypes.c_void_p(q.data_ptr()),
-            ctypes.c_void_p(k.data_ptr()), ctypes.c_void_p(self._ws_ptr),
-            ctypes.c_size_t(nbytes), ctypes.c_void_p(_stream_ptr(stream)),
-            ctypes.byref(self._handle))
-        _lib.check(st, "sparse_attn_plan")
+        if _launch is None:
+            st = lib.sparse_attn_plan(
+                ctypes.byref(self.params), ctypes.c_void_p(q.data_ptr()),
+                ctypes.c_void_p(k.data_ptr()), ctypes.c_void_p(self._ws_ptr),
+                ctypes.c_size_t(nbytes), ctypes.c_void_p(_stream_ptr(stream)),
+                ctypes.byref(self._handle))
+            _lib.check(st, "sparse_attn_plan")
+        else:  # a call that builds the plan itself (sparse_attn_forward)
+            _launch(self, nbytes)
 
     @property
     def tau(self) -> float:
@@ -193,6 +198,42 @@ def plan(q: torch.Tensor, k: torch.Tensor, segment: int, tau: float,
          block: int = 64, flags: int = 0, stream=None) -> SparsePlan:
     """Importance estimation and index building (sparse_attn_plan)."""
     return SparsePlan(q, k, segment, tau, block, flags, stream)
+
+
+def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, segment: int,
+            tau: float, block: int = 64, flags: int = 0,
+            out: Optional[torch.Tensor] = None, return_lse: bool = False,
+            stream=None, side_stream=None):
+    """Plan and prefill in one call (sparse_attn_forward): the dense local
+    windows run on `side_stream` (a second stream of the same device; None:
+    the plan and the attention one after the other on `stream`) while the
+    planner runs on `stream`. Returns (plan, o) or (plan, o, lse); the plan
+    serves the setters, exports and later prefills as from plan()."""
+    lib = _lib.load()
+    for x, n in ((q, "q"), (k, "k"), (v, "v")):
+        _check_tensor(x, n)
+    if k.shape != v.shape:
+        raise ValueError("k and v shapes do not agree")
+    o = out if out is not None else torch.empty_like(q)
+    _check_tensor(o, "out")
+    lse = (torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+           if return_lse else None)
+    main = _stream_ptr(stream)
+    side = _stream_ptr(side_stream) if side_stream is not None else main
+
+    def launch(pl, nbytes):
+        st = lib.sparse_attn_forward(
+            ctypes.byref(pl.params), ctypes.c_void_p(q.data_ptr()),
+            ctypes.c_void_p(k.data_ptr()), ctypes.c_void_p(v.data_ptr()),
+            ctypes.c_void_p(o.data_ptr()),
+            ctypes.c_void_p(lse.data_ptr() if lse is not None else 0),
+            ctypes.c_void_p(pl._ws_ptr), ctypes.c_size_t(nbytes),
+            ctypes.c_void_p(main), ctypes.c_void_p(side),
+            ctypes.byref(pl._handle))
+        _lib.check(st, "sparse_attn_forward")
+
+    pl = SparsePlan(q, k, segment, tau, block, flags, stream, _launch=launch)
+    return (pl, o, lse) if return_lse else (pl, o)
 
 
 def prefill(pl: SparsePlan, q: torch.Tensor, k: torch.Tensor,

@@ -32,6 +32,7 @@ SA_EXPORT_POOLED = 7
 
 EXPORTED_SYMBOLS = (
     "sparse_attn_workspace_bytes", "sparse_attn_plan", "sparse_attn_prefill",
+    "sparse_attn_forward",
     "sparse_attn_plan_set_tau", "sparse_attn_plan_set_budget",
     "sparse_attn_plan_set_max_threshold",
     "sparse_attn_plan_export_bytes",
@@ -76,6 +77,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.sparse_attn_plan.restype = i32
     lib.sparse_attn_prefill.argtypes = [vp, vp, vp, vp, vp, vp, vp]
     lib.sparse_attn_prefill.restype = i32
+    lib.sparse_attn_forward.argtypes = [P, vp, vp, vp, vp, vp, vp, sz, vp, vp,
+                                        ctypes.POINTER(vp)]
+    lib.sparse_attn_forward.restype = i32
     lib.sparse_attn_plan_set_tau.argtypes = [vp, ctypes.c_double]
     lib.sparse_attn_plan_set_tau.restype = i32
     lib.sparse_attn_plan_set_budget.argtypes = [vp, i32]

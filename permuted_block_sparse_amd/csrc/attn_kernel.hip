@@ -651,12 +651,16 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_fwd(AttnArgs a) {
 
 int attention_blocks_per_wg() { return 4; }
 
-hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
+hipError_t launch_attention_local(const AttnArgs& a, hipStream_t s) {
   const int total = a.n_groups * a.wg_per_group;
   // the dense local windows in the rows' own order
   hipLaunchKernelGGL(k_attn_fwd<kLocal>, dim3(total), dim3(kThreads), 0, s, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || a.local_only) return e;
+  return hipGetLastError();
+}
+
+hipError_t launch_attention_sparse(const AttnArgs& a, hipStream_t s) {
+  if (a.local_only) return hipSuccess;
+  const int total = a.n_groups * a.wg_per_group;
   if (a.exact) {
     hipLaunchKernelGGL(k_attn_fwd<kExactMax>, dim3(total), dim3(kThreads), 0,
                        s, a);
@@ -665,7 +669,7 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
   // the bounded workgroups, then (flagged by the first launch) the others
   hipLaunchKernelGGL(k_attn_fwd<kFastRef>, dim3(total), dim3(kThreads), 0, s,
                      a);
-  e = hipGetLastError();
+  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_attn_fwd<kMaxRef>, dim3(total), dim3(kThreads), 0, s,
                      a);

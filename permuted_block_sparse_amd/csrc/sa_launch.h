@@ -110,7 +110,11 @@ struct AttnArgs {
   int exact;       // 1: exact per-block max test instead of the stop points
   float exact_thr; // that test's threshold on the raw dot products (theta / kappa)
 };
-hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
+// The local pass (every row's dense local window, rows in their own order;
+// needs nothing from the plan but its workspace) and the sparse passes
+// (after the local pass and the stop points).
+hipError_t launch_attention_local(const AttnArgs& a, hipStream_t s);
+hipError_t launch_attention_sparse(const AttnArgs& a, hipStream_t s);
 // Query blocks one attention workgroup processes (sets wg_per_group).
 int attention_blocks_per_wg();
 

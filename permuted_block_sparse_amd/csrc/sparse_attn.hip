@@ -243,9 +243,11 @@ size_t sparse_attn_workspace_bytes(const sa_params* p) {
   return layout_of(dims_of(p)).total;
 }
 
-int sparse_attn_plan(const sa_params* p, const void* q, const void* k,
-                     void* workspace, size_t workspace_bytes,
-                     hipStream_t stream, sa_plan** out) {
+namespace {
+
+// Validation and the plan object (host only; no launch).
+int plan_create(const sa_params* p, const void* q, const void* k,
+                void* workspace, size_t workspace_bytes, sa_plan** out) {
   if (out == nullptr) return SA_ERR_NULL_POINTER;
   *out = nullptr;
   const int st = validate(p);
@@ -257,7 +259,6 @@ int sparse_attn_plan(const sa_params* p, const void* q, const void* k,
   const PlanDims d = dims_of(p);
   const Layout lay = layout_of(d);
   if (workspace_bytes < lay.total) return SA_ERR_WORKSPACE_TOO_SMALL;
-
   sa_plan* pl = new (std::nothrow) sa_plan;
   if (pl == nullptr) return SA_ERR_HOST_ALLOC;
   pl->p = *p;
@@ -266,9 +267,18 @@ int sparse_attn_plan(const sa_params* p, const void* q, const void* k,
   pl->ws = static_cast<char*>(workspace);
   pl->q = q;
   pl->k = k;
+  *out = pl;
+  return SA_OK;
+}
 
-  const uint16_t* qb = static_cast<const uint16_t*>(q);
-  const uint16_t* kb = static_cast<const uint16_t*>(k);
+// Every planner kernel of a new plan: pooling, scores, both orders, the
+// restricted lists, the contrast vectors, the stop points.
+int plan_launch(sa_plan* pl, hipStream_t stream) {
+  const PlanDims& d = pl->d;
+  const Layout& lay = pl->lay;
+  const sa_params* p = &pl->p;
+  const uint16_t* qb = static_cast<const uint16_t*>(pl->q);
+  const uint16_t* kb = static_cast<const uint16_t*>(pl->k);
   hipError_t e = launch_pool_q(d, qb, pl->at<int64_t>(lay.pool_part), stream);
   if (e == hipSuccess)
     e = launch_pool_reduce(d, pl->at<int64_t>(lay.pool_part),
@@ -303,20 +313,12 @@ int sparse_attn_plan(const sa_params* p, const void* q, const void* k,
   int rc = hip_status(e);
   if (rc == SA_OK) rc = build_from_kv_order(pl, stream);
   if (rc == SA_OK) rc = run_stop_scan(pl, stream);
-  if (rc != SA_OK) {
-    delete pl;
-    return rc;
-  }
-  *out = pl;
-  return SA_OK;
+  return rc;
 }
 
-int sparse_attn_prefill(const sa_plan* plan, const void* q, const void* k,
-                        const void* v, void* o, float* lse,
-                        hipStream_t stream) {
-  if (plan == nullptr || q == nullptr || k == nullptr || v == nullptr ||
-      o == nullptr)
-    return SA_ERR_NULL_POINTER;
+// The attention launches' arguments for the plan's current settings.
+AttnArgs attn_args(const sa_plan* plan, const void* q, const void* k,
+                   const void* v, void* o, float* lse) {
   const PlanDims& d = plan->d;
   AttnArgs a;
   a.q = static_cast<const uint16_t*>(q);
@@ -354,12 +356,91 @@ int sparse_attn_prefill(const sa_plan* plan, const void* q, const void* k,
   a.border = (!a.exact && block_order_used(d))
                  ? plan->at<int32_t>(plan->lay.border)
                  : nullptr;
+  return a;
+}
+
+// The sparse passes, after rescanning stale stop points.
+int sparse_passes(const sa_plan* plan, const AttnArgs& a, hipStream_t stream) {
   if (!a.exact && !plan->stops_valid) {
     const int rc = run_stop_scan(plan, stream);
     if (rc != SA_OK) return rc;
   }
   if (a.exact) plan->stops_valid = false;
-  return hip_status(launch_attention(a, stream));
+  return hip_status(launch_attention_sparse(a, stream));
+}
+
+}  // namespace
+
+int sparse_attn_plan(const sa_params* p, const void* q, const void* k,
+                     void* workspace, size_t workspace_bytes,
+                     hipStream_t stream, sa_plan** out) {
+  if (out == nullptr) return SA_ERR_NULL_POINTER;
+  *out = nullptr;
+  sa_plan* pl = nullptr;
+  int rc = plan_create(p, q, k, workspace, workspace_bytes, &pl);
+  if (rc != SA_OK) return rc;
+  rc = plan_launch(pl, stream);
+  if (rc != SA_OK) {
+    delete pl;
+    return rc;
+  }
+  *out = pl;
+  return SA_OK;
+}
+
+int sparse_attn_prefill(const sa_plan* plan, const void* q, const void* k,
+                        const void* v, void* o, float* lse,
+                        hipStream_t stream) {
+  if (plan == nullptr || q == nullptr || k == nullptr || v == nullptr ||
+      o == nullptr)
+    return SA_ERR_NULL_POINTER;
+  const AttnArgs a = attn_args(plan, q, k, v, o, lse);
+  const int rc = hip_status(launch_attention_local(a, stream));
+  if (rc != SA_OK) return rc;
+  return sparse_passes(plan, a, stream);
+}
+
+int sparse_attn_forward(const sa_params* p, const void* q, const void* k,
+                        const void* v, void* o, float* lse, void* workspace,
+                        size_t workspace_bytes, hipStream_t stream,
+                        hipStream_t side_stream, sa_plan** out) {
+  if (out == nullptr) return SA_ERR_NULL_POINTER;
+  *out = nullptr;
+  if (v == nullptr || o == nullptr) return SA_ERR_NULL_POINTER;
+  sa_plan* pl = nullptr;
+  int rc = plan_create(p, q, k, workspace, workspace_bytes, &pl);
+  if (rc != SA_OK) return rc;
+  const AttnArgs a = attn_args(pl, q, k, v, o, lse);
+  if (side_stream == stream) {  // one stream: plan, then prefill
+    rc = plan_launch(pl, stream);
+    if (rc == SA_OK) rc = hip_status(launch_attention_local(a, stream));
+    if (rc == SA_OK) rc = sparse_passes(pl, a, stream);
+  } else {
+    // the local pass (which needs none of the plan's results) on the side
+    // stream while the planner runs on `stream`; the sparse passes wait for
+    // both
+    hipEvent_t ready = nullptr, local_done = nullptr;
+    hipError_t e = hipEventCreateWithFlags(&ready, hipEventDisableTiming);
+    if (e == hipSuccess)
+      e = hipEventCreateWithFlags(&local_done, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventRecord(ready, stream);
+    if (e == hipSuccess) e = hipStreamWaitEvent(side_stream, ready, 0);
+    if (e == hipSuccess) e = launch_attention_local(a, side_stream);
+    if (e == hipSuccess) e = hipEventRecord(local_done, side_stream);
+    rc = hip_status(e);
+    if (rc == SA_OK) rc = plan_launch(pl, stream);
+    if (rc == SA_OK) rc = hip_status(hipStreamWaitEvent(stream, local_done, 0));
+    if (rc == SA_OK) rc = sparse_passes(pl, a, stream);
+    // released once the work recorded on them has completed
+    if (ready != nullptr) hipEventDestroy(ready);
+    if (local_done != nullptr) hipEventDestroy(local_done);
+  }
+  if (rc != SA_OK) {
+    delete pl;
+    return rc;
+  }
+  *out = pl;
+  return SA_OK;
 }
 
 int sparse_attn_plan_set_max_threshold(sa_plan* plan, double theta) {

@@ -25,7 +25,7 @@ def declared_functions():
 def test_every_declared_symbol_is_exported():
     lib = _lib.load()
     names = declared_functions()
-    assert len(names) == 11
+    assert len(names) == 12
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(_lib.EXPORTED_SYMBOLS)
@@ -74,6 +74,27 @@ def test_plan_rejects_before_launch():
     assert out.value is None
     assert lib.sparse_attn_plan(ctypes.byref(p), fake, fake, fake, n, None,
                                 None) == _lib.SA_ERR_NULL_POINTER
+
+
+def test_forward_rejects_before_launch():
+    """sparse_attn_forward checks its own arguments and the plan's before it
+    enqueues anything."""
+    lib = _lib.load()
+    f = ctypes.c_void_p(1 << 20)
+    p = P()
+    n = lib.sparse_attn_workspace_bytes(ctypes.byref(p))
+    out = ctypes.c_void_p()
+    assert lib.sparse_attn_forward(ctypes.byref(p), f, f, f, f, None, f, n,
+                                   None, None, None) == \
+        _lib.SA_ERR_NULL_POINTER
+    for args in ((f, f, None, f), (f, f, f, None), (None, f, f, f)):
+        assert lib.sparse_attn_forward(ctypes.byref(p), *args, None, f, n,
+                                       None, None, ctypes.byref(out)) == \
+            _lib.SA_ERR_NULL_POINTER
+    assert lib.sparse_attn_forward(ctypes.byref(p), f, f, f, f, None, f,
+                                   n - 1, None, None, ctypes.byref(out)) == \
+        _lib.SA_ERR_WORKSPACE_TOO_SMALL
+    assert out.value is None
 
 
 def test_other_entry_points_reject_null():

@@ -155,6 +155,39 @@ def test_reference_paths():
     assert_outputs_close(g["o"], od, g["lse"], ld)
 
 
+def test_forward_matches_plan_then_prefill():
+    """sparse_attn_forward (local windows on a second stream while the
+    planner runs) returns what plan + prefill return, bit for bit, and so
+    does its one-stream form; the plan it returns serves a further prefill
+    at another tau."""
+    import torch
+    import permuted_block_sparse_amd as pbs
+    from tests.gpu_helpers import to_device
+    spec = _spec(1, 4, 1, 4096, 43, n_vert=32, window=128)
+    q, k, v = make_stripe_inputs(spec)
+    tq, tk, tv = to_device(q), to_device(k), to_device(v)
+    S, tau = 512, 0.05
+    pl = pbs.plan(tq, tk, S, tau)
+    o_ref, l_ref = pbs.prefill(pl, tq, tk, tv, return_lse=True)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    for name, ss in (("side stream", side), ("one stream", None)):
+        say(f"[forward] {name}")
+        pf, o, l = pbs.forward(tq, tk, tv, S, tau, return_lse=True,
+                               side_stream=ss)
+        torch.cuda.synchronize()
+        assert torch.equal(o.view(torch.int16), o_ref.view(torch.int16))
+        assert torch.equal(l, l_ref)
+        for ex in ("pi_k", "pi_q", "restricted_lists", "n_I"):
+            assert np.array_equal(getattr(pf, ex)(), getattr(pl, ex)()), ex
+    pf.set_tau(0.2)
+    pl.set_tau(0.2)
+    o2 = pbs.prefill(pf, tq, tk, tv)
+    o2_ref = pbs.prefill(pl, tq, tk, tv)
+    torch.cuda.synchronize()
+    assert torch.equal(o2.view(torch.int16), o2_ref.view(torch.int16))
+
+
 def test_tau0_is_dense_and_kv_order_invariant():
     spec = _spec(1, 4, 2, 1024, 31)
     q, k, v = make_stripe_inputs(spec)

@@ -432,8 +432,8 @@ int sparse_attn_forward(const sa_params* p, const void* q, const void* k,
     if (rc == SA_OK) rc = hip_status(hipStreamWaitEvent(stream, local_done, 0));
     if (rc == SA_OK) rc = sparse_passes(pl, a, stream);
     // released once the work recorded on them has completed
-    if (ready != nullptr) hipEventDestroy(ready);
-    if (local_done != nullptr) hipEventDestroy(local_done);
+    if (ready != nullptr) (void)hipEventDestroy(ready);
+    if (local_done != nullptr) (void)hipEventDestroy(local_done);
   }
   if (rc != SA_OK) {
     delete pl;

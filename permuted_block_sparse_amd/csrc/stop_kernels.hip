@@ -55,17 +55,21 @@ static __device__ __forceinline__ void sum_rows64(const uint16_t* base,
                                            int row_of_lane, int lane,
                                            float (&s)[8]) {
   const int c = lane & 15, rg = lane >> 4;
-  uint4 w[16];
-#pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    const int row = __shfl(row_of_lane, rg + 4 * j);
-    w[j] = *reinterpret_cast<const uint4*>(base + (size_t)row * kHeadDim +
-                                           8 * c);
-  }
 #pragma unroll
   for (int e = 0; e < 8; ++e) s[e] = 0.f;
+  // two batches of 8 loads (fewer registers held), added in row order
 #pragma unroll
-  for (int j = 0; j < 16; ++j) add_bf16x8(s, w[j]);
+  for (int h = 0; h < 2; ++h) {
+    uint4 w[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int row = __shfl(row_of_lane, rg + 4 * (8 * h + j));
+      w[j] = *reinterpret_cast<const uint4*>(base + (size_t)row * kHeadDim +
+                                             8 * c);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) add_bf16x8(s, w[j]);
+  }
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     s[e] += __shfl_xor(s[e], 16);
@@ -154,9 +158,6 @@ __global__ __launch_bounds__(kScanThreads) void k_stop_scan(StopArgs a) {
   }
   const int seg0 = t * a.S;
   const int32_t* pq = a.pi_q + bh * a.N + (long long)I * kBlock + 16 * dq;
-  int rofs[16];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) rofs[i] = min(max(pq[i], 0), a.N - 1) - seg0;
 
   const uint16_t* kbase = a.k + (long long)bg * a.N * kHeadDim;
   const int32_t* Lt = a.L + (long long)bg * a.list_len +
@@ -206,6 +207,11 @@ __global__ __launch_bounds__(kScanThreads) void k_stop_scan(StopArgs a) {
     load_sums(true, c0, cnt);
     __syncthreads();
     if (valid) {
+      // this thread's 16 rows (offsets from the segment start)
+      int rofs[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        rofs[i] = min(max(pq[i], 0), a.N - 1) - seg0;
       for (int kk = 0; kk < cnt; ++kk) {
         const int j0 = (c0 + kk) * kBlock;
         int nv = 0;

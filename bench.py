@@ -59,6 +59,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-once", action="store_true",
                     help="one plan + one prefill, no timing (counter runs)")
+    ap.add_argument("--plan-only", type=int, default=0, metavar="K",
+                    help="only K plans after one warm-up plan (planner "
+                         "kernel traces; no attention)")
     ap.add_argument("--copy-calibration", type=int, default=0,
                     metavar="MIB",
                     help="only copy MIB MiB device->device (a plain copy "
@@ -122,6 +125,12 @@ def main():
         step()
         torch.cuda.synchronize()
         log("[bench] one plan + prefill done")
+        return
+    if args.plan_only:
+        for i in range(args.plan_only + 1):
+            pbs.plan(tq, tk, S, tau)
+            torch.cuda.synchronize()
+        log(f"[bench] {args.plan_only} plans done")
         return
 
     for i in range(args.warmup):

@@ -615,9 +615,6 @@ __global__ __launch_bounds__(256) void k_restrict_write(
 }
 
 // --------------------------------------------------------------------------
-// Launchers
-// --------------------------------------------------------------------------
-// --------------------------------------------------------------------------
 // Segment-local key order (the PBS-Attn page's permutation inside causal
 // segments): pi_K sorts the keys of each segment by v; its 64-key chunks are
 // the tiles; segment t visits the tiles of segments 0 .. t - 1 by tile score
@@ -675,6 +672,9 @@ __global__ __launch_bounds__(256) void k_segment_tiles(
     Lt[i] = pk[idx[i >> 6] * 64 + (i & 63)];
 }
 
+// --------------------------------------------------------------------------
+// Launchers
+// --------------------------------------------------------------------------
 hipError_t launch_pool_q(const PlanDims& d, const uint16_t* q, int64_t* part,
                          hipStream_t s) {
   hipLaunchKernelGGL(k_pool_q, dim3(d.B * d.Hq * d.n_pool_chunks), dim3(256), 0,

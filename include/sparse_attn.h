@@ -21,6 +21,9 @@
  *                           query block at its stop point, and the scatter
  *                           of each output row back to its original
  *                           position.
+ * sparse_attn_forward makes both in one call, overlapping the prefill's
+ * dense local windows (which need only q, k, v) with the plan on a second
+ * stream.
  *
  * Conventions for every entry point:
  *   - Tensors are caller-owned DEVICE pointers, bfloat16 (raw 16-bit
@@ -30,13 +33,14 @@
  *   - Work is enqueued on the caller's stream and runs asynchronously; no
  *     entry point synchronizes except sparse_attn_plan_export.
  *   - Every argument is validated before anything is launched; a call that
- *     returns an error has launched nothing and changed nothing.
+ *     returns a validation error has launched nothing and changed nothing.
  *   - Status codes, never exceptions or aborts. A HIP launch failure is
- *     reported as SA_ERR_HIP; errors of earlier asynchronous work may
- *     surface there too. Non-finite inputs give unspecified (but memory-safe)
- *     results.
+ *     reported as SA_ERR_HIP (work launched before it stays enqueued);
+ *     errors of earlier asynchronous work may surface there too. Non-finite
+ *     inputs give unspecified (but memory-safe) results.
  *   - No global state: all device scratch lives in the caller's workspace.
- *     A plan must not be used on two streams at once.
+ *     A plan must not be used on two streams at once (sparse_attn_forward
+ *     orders its own two streams).
  */
 #ifndef SPARSE_ATTN_H
 #define SPARSE_ATTN_H

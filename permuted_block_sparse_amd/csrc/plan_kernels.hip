@@ -76,6 +76,32 @@ __global__ __launch_bounds__(1024) void k_pool_reduce(
   }
 }
 
+// An int64 factor c of the stripe scores as c = lo + hi 2^32 with lo the
+// signed low word: fx (|fx| <= 2^15) times c is then one 32 x 32 -> 64-bit
+// multiply-add and one 24-bit one, exactly. The pooled query (|P| <= 2^40:
+// G <= 256, N <= 2^17) and C_t (|C| <= 2^39) leave |hi| <= 2^8.
+struct Split64 {
+  int32_t lo, hi;
+};
+__device__ __forceinline__ Split64 split64(int64_t c) {
+  Split64 r;
+  r.lo = (int32_t)(uint32_t)(uint64_t)c;
+  r.hi = (int32_t)((c - (int64_t)r.lo) >> 32);
+  return r;
+}
+// sum over e of f[e] c[e], exact in int64
+__device__ __forceinline__ int64_t dot8_split(const int32_t (&f)[8],
+                                              const Split64 (&c)[8]) {
+  int64_t lo = 0;
+  int32_t hi = 0;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    lo += (int64_t)f[e] * c[e].lo;
+    hi += __mul24(f[e], c[e].hi);  // both within 24 bits
+  }
+  return lo + ((int64_t)hi << 32);
+}
+
 // --------------------------------------------------------------------------
 // Key stripe score v_j = pooled . fx(k_j) (int64) and, on the same pass over
 // K, the per-64-row column sums of fx(k) (int32; |sum| <= 64 * 2^15) and the
@@ -92,9 +118,10 @@ __global__ __launch_bounds__(256) void k_key_score(
   const int tid = threadIdx.x, c = tid & 15, rr = tid >> 4;
   const int row0 = w * kScoreRows;
   const int rows = min(kScoreRows, N - row0);  // a multiple of 64
-  int64_t p8[8];
+  Split64 p8[8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) p8[e] = pooled[(size_t)bg * kHeadDim + c * 8 + e];
+  for (int e = 0; e < 8; ++e)
+    p8[e] = split64(pooled[(size_t)bg * kHeadDim + c * 8 + e]);
   const uint16_t* base = k + ((size_t)bg * N + row0) * kHeadDim + c * 8;
   int32_t bs[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   float kn = 0.f;  // largest |k|^2 of this thread's rows
@@ -104,12 +131,9 @@ __global__ __launch_bounds__(256) void k_key_score(
       uint4 wv = *reinterpret_cast<const uint4*>(base + (size_t)r * kHeadDim);
       int32_t f[8];
       fixed_point8(wv, f);
-      int64_t dot = 0;
+      int64_t dot = dot8_split(f, p8);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        dot += (int64_t)f[e] * p8[e];
-        bs[e] += f[e];
-      }
+      for (int e = 0; e < 8; ++e) bs[e] += f[e];
       dot = sum16_i64(dot);
       if (c == 0) vscore[(size_t)bg * N + row0 + r] = dot;
       const uint32_t wd[4] = {wv.x, wv.y, wv.z, wv.w};
@@ -237,22 +261,20 @@ __global__ __launch_bounds__(256) void k_query_score(
   const uint16_t* base = q + ((size_t)bh * N + row0) * kHeadDim + c * 8;
   // this lane's 8 entries of C_t, reloaded when the segment changes
   int t_loaded = -1;
-  int64_t cv[8];
+  Split64 cv[8];
   for (int p = 0; p * 16 < rows; ++p) {
     const int r = rr + 16 * p;
     const int t = (row0 + r) / S;
     if (t != t_loaded) {
       const int64_t* src = contrast + ((size_t)bg * T + t) * kHeadDim + c * 8;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) cv[e] = src[e];
+      for (int e = 0; e < 8; ++e) cv[e] = split64(src[e]);
       t_loaded = t;
     }
     uint4 wv = *reinterpret_cast<const uint4*>(base + (size_t)r * kHeadDim);
     int32_t f[8];
     fixed_point8(wv, f);
-    int64_t dot = 0;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) dot += (int64_t)f[e] * cv[e];
+    int64_t dot = dot8_split(f, cv);
     dot = row16_sum_i64(dot);
     if (c == 15) u[(size_t)bh * N + row0 + r] = dot;
   }

@@ -422,6 +422,39 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_fwd(AttnArgs a) {
   const uint16_t* kbase = a.k + (size_t)bg * a.N * kHeadDim;
   const uint16_t* vbase = a.v + (size_t)bg * a.N * kHeadDim;
 
+  // ---- the step sequence: the local pass's ndiag key blocks of the
+  // segment, or the sparse passes' tiles of L_t up to the largest stop point
+  // of the workgroup's blocks.
+  const int ntl = t * bps;  // tiles of L_t
+  int32_t* nI_ptr = a.n_I + bh * (a.N / kBlock) + I;
+  const int nI = (!valid || kLoc) ? 0 : kExact ? ntl : min(max(*nI_ptr, 0), ntl);
+  const int32_t* Lt =
+      a.L + (size_t)bg * a.list_len + (size_t)a.S * t * (t - 1) / 2;
+  // sparse passes: no local step (the local pass covered those blocks);
+  // a.local_steps is 0, read at run time as a value in [0, 1]: with a
+  // literal 0 (or an unbounded value) the compiler schedules the loop with
+  // more registers and spills
+  const int ndiag_sparse = a.local_steps != 0 ? 1 : 0;
+
+  // The first three tiles' rows are requested before the step count is
+  // known (that takes a barrier), so their latency overlaps the query rows'
+  // and the barrier: the local pass's tiles are the segment's first key
+  // blocks, a sparse pass's the first tiles of L_t (indices clamped into a
+  // non-empty L_t; a workgroup of the first segment has no sparse tile and
+  // reads none). Rows of steps beyond the count are loaded and never used.
+  const int rg = gather_row(wave, lane);
+  const StoreAddr sta = store_addr(rg, lane);
+  const ReadAddr ra = read_addr(lane);
+  auto first_key = [&](int s) -> int {
+    if (kLoc || s < ndiag_sparse || ntl == 0) return seg0 + s * kBlock + rg;
+    const int k = min(s - ndiag_sparse, max(ntl - 1, 0));
+    return Lt[(size_t)k * kBlock + rg];
+  };
+  const Staged r0 = load_rows(kbase, vbase, first_key(0), a.N, lane);
+  const Staged r1 = load_rows(kbase, vbase, first_key(1), a.N, lane);
+  Staged nxt = load_rows(kbase, vbase, first_key(2), a.N, lane);
+  int raw = kLoc ? 0 : first_key(3);
+
   // the lane's query row as Q^T B operands, for the whole run
   bf16x8 qr[8];
 #pragma unroll
@@ -455,12 +488,6 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_fwd(AttnArgs a) {
     l = 1.f;
   }
 
-  // ---- the step sequence: the local pass's ndiag key blocks of the
-  // segment, or the sparse passes' tiles of L_t up to the largest stop point
-  // of the workgroup's blocks.
-  const int ntl = t * bps;  // tiles of L_t
-  int32_t* nI_ptr = a.n_I + bh * (a.N / kBlock) + I;
-  const int nI = (!valid || kLoc) ? 0 : kExact ? ntl : min(max(*nI_ptr, 0), ntl);
   const int myrow = wave_max_int(iq);
   if (lane == 0) {
     wave_maxrow[wave] = valid ? myrow : -1;
@@ -473,28 +500,20 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_fwd(AttnArgs a) {
     wgmax = max(wgmax, wave_maxrow[w]);
     ntiles = max(ntiles, wave_ntiles[w]);
   }
-  // sparse passes: no local step (the local pass covered those blocks);
-  // a.local_steps is 0, read at run time as a value in [0, 1]: with a
-  // literal 0 (or an unbounded value) the compiler schedules the loop with
-  // more registers and spills
   const int ndiag = kLoc ? min(max((wgmax - seg0) / kBlock + 1, 1), bps)
-                         : (a.local_steps != 0 ? 1 : 0);
+                         : ndiag_sparse;
   const int nsteps = ndiag + ntiles;
   if (!kLoc && ntiles == 0) {
     // no sparse tile: the local pass's output and lse are final
     if (kFast && tid == 0) a.wg_flag[blockIdx.x] = 0;
     if (kExact && valid && lane == 0 && half == 0) *nI_ptr = 0;
+    __builtin_amdgcn_s_waitcnt(0);  // the first tiles' loads
     return;
   }
-  const int32_t* Lt =
-      a.L + (size_t)bg * a.list_len + (size_t)a.S * t * (t - 1) / 2;
 
   // Tile indices: every step loads the index of the row this lane gathers
   // three steps later (local steps load a harmless in-bounds value and
   // compute their indices instead).
-  const int rg = gather_row(wave, lane);
-  const StoreAddr sta = store_addr(rg, lane);
-  const ReadAddr ra = read_addr(lane);
   auto key_src = [&](int s, int row) -> const int32_t* {
     return (s >= ndiag && s < nsteps) ? Lt + (size_t)(s - ndiag) * kBlock + row
                                       : pq + (row & 63);
@@ -513,14 +532,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_fwd(AttnArgs a) {
   // s - 1, and the loads of tile s + 3's rows and tile s + 4's indices are
   // issued. One barrier per step. A wave whose block has stopped (or whose
   // tile the exact test rejects) runs the same instructions as a no-op.
-  {
-    const Staged r0 = stage(0, *key_src(0, rg));
-    const Staged r1 = stage(1, *key_src(1, rg));
-    store_rows(tiles[0], tiles[0] + kTileBytes, r0, sta);
-    store_rows(tiles[1], tiles[1] + kTileBytes, r1, sta);
-  }
-  Staged nxt = stage(2, *key_src(2, rg));
-  int raw = *key_src(3, rg);
+  store_rows(tiles[0], tiles[0] + kTileBytes, r0, sta);
+  store_rows(tiles[1], tiles[1] + kTileBytes, r1, sta);
   __syncthreads();
   f32x16 sa[2], sb[2];
   qk_tile(tiles[0], qr, sa, ra);

@@ -62,6 +62,10 @@ def parse():
     ap.add_argument("--plan-only", type=int, default=0, metavar="K",
                     help="only K plans after one warm-up plan (planner "
                          "kernel traces; no attention)")
+    ap.add_argument("--prefill-only", type=int, default=0, metavar="K",
+                    help="one plan, then K prefills of it after one warm-up "
+                         "prefill (attention kernel traces; no planner "
+                         "kernel runs beside them)")
     ap.add_argument("--copy-calibration", type=int, default=0,
                     metavar="MIB",
                     help="only copy MIB MiB device->device (a plain copy "
@@ -131,6 +135,22 @@ def main():
             pbs.plan(tq, tk, S, tau)
             torch.cuda.synchronize()
         log(f"[bench] {args.plan_only} plans done")
+        return
+    if args.prefill_only:
+        pl = pbs.plan(tq, tk, S, tau)
+        pbs.prefill(pl, tq, tk, tv, out=out)
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(args.prefill_only):
+            a_ = torch.cuda.Event(enable_timing=True)
+            b_ = torch.cuda.Event(enable_timing=True)
+            a_.record(stream)
+            pbs.prefill(pl, tq, tk, tv, out=out)
+            b_.record(stream)
+            torch.cuda.synchronize()
+            ts.append(a_.elapsed_time(b_))
+        log(f"[bench] {args.prefill_only} prefills alone: mean "
+            f"{float(np.mean(ts)):.3f} ms (HIP events)")
         return
 
     for i in range(args.warmup):

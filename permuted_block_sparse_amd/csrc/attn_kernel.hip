@@ -400,6 +400,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_fwd(AttnArgs a) {
   const int t = a.T - 1 - grp / BH;
   const int bg = grp % BH, b = bg / a.Hkv, g = bg % a.Hkv;
   const int bps = a.S / kBlock;  // query blocks per segment and head
+  const int seg0 = t * a.S;
   // query block e of the group: in order (local pass), or the sparse pass's
   // order by stop point
   const int ewg = chunk * 4 + qsub;
@@ -407,27 +408,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_fwd(AttnArgs a) {
   const int e = (!kLoc && a.border != nullptr && valid)
                     ? a.border[((long long)bg * a.T + t) * (a.G * bps) + ewg]
                     : ewg;
-  const int h = g * a.G + (valid ? e % a.G : 0);
-  const int Ib = valid ? e / a.G : 0;  // block index within the segment
-  const int I = t * bps + Ib;
-  const int seg0 = t * a.S;
-
-  const size_t bh = (size_t)b * a.Hq + h;
-  const int32_t* pq = a.pi_q + bh * a.N + (size_t)I * kBlock;
-  // my row: the local pass takes the segment's rows in their own order,
-  // the sparse passes the rows of block I of pi_Q
-  const int iq = kLoc ? seg0 + Ib * kBlock + 32 * half + lq
-                      : min(max(pq[32 * half + lq], 0), a.N - 1);
-  const uint16_t* qh = a.q + bh * a.N * kHeadDim;
-  const uint16_t* kbase = a.k + (size_t)bg * a.N * kHeadDim;
-  const uint16_t* vbase = a.v + (size_t)bg * a.N * kHeadDim;
 
   // ---- the step sequence: the local pass's ndiag key blocks of the
   // segment, or the sparse passes' tiles of L_t up to the largest stop point
   // of the workgroup's blocks.
   const int ntl = t * bps;  // tiles of L_t
-  int32_t* nI_ptr = a.n_I + bh * (a.N / kBlock) + I;
-  const int nI = (!valid || kLoc) ? 0 : kExact ? ntl : min(max(*nI_ptr, 0), ntl);
   const int32_t* Lt =
       a.L + (size_t)bg * a.list_len + (size_t)a.S * t * (t - 1) / 2;
   // sparse passes: no local step (the local pass covered those blocks);
@@ -437,23 +422,47 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_fwd(AttnArgs a) {
   const int ndiag_sparse = a.local_steps != 0 ? 1 : 0;
 
   // The first three tiles' rows are requested before the step count is
-  // known (that takes a barrier), so their latency overlaps the query rows'
-  // and the barrier: the local pass's tiles are the segment's first key
-  // blocks, a sparse pass's the first tiles of L_t (indices clamped into a
-  // non-empty L_t; a workgroup of the first segment has no sparse tile and
-  // reads none). Rows of steps beyond the count are loaded and never used.
+  // known (that takes a barrier): the local pass's tiles are the segment's
+  // first key blocks, a sparse pass's the first tiles of L_t (indices
+  // clamped into a non-empty L_t; a workgroup of the first segment has no
+  // sparse tile and reads pi_Q instead). Rows of steps beyond the count are
+  // loaded and never used. The index loads go out with the block-order load, as
+  // neither depends on the other, and the row loads before the loads that
+  // wait for the block's rows: three dependent memory round trips before
+  // the first tile (block order, pi_Q, query rows; indices, key rows) where
+  // a plain order of the statements makes seven.
   const int rg = gather_row(wave, lane);
+  // (branch-free, so that no wait for an index load sits between them)
+  auto first_key = [&](int s) -> int {
+    const bool computed = kLoc || s < ndiag_sparse || ntl == 0;
+    const int k = min(max(s - ndiag_sparse, 0), max(ntl - 1, 0));
+    const int32_t* src = ntl == 0 ? a.pi_q + rg : Lt + (size_t)k * kBlock + rg;
+    const int x = kLoc ? 0 : *src;
+    return computed ? seg0 + s * kBlock + rg : x;
+  };
+  const int key0 = first_key(0), key1 = first_key(1), key2 = first_key(2);
+  int raw = kLoc ? 0 : first_key(3);
+
+  const int h = g * a.G + (valid ? e % a.G : 0);
+  const int Ib = valid ? e / a.G : 0;  // block index within the segment
+  const int I = t * bps + Ib;
+  const size_t bh = (size_t)b * a.Hq + h;
+  const int32_t* pq = a.pi_q + bh * a.N + (size_t)I * kBlock;
+  int32_t* nI_ptr = a.n_I + bh * (a.N / kBlock) + I;
+  const int nI_raw = *nI_ptr;  // unconditional: no wait for it until used
+  const int nI = (!valid || kLoc) ? 0 : kExact ? ntl : min(max(nI_raw, 0), ntl);
+  // my row: the local pass takes the segment's rows in their own order,
+  // the sparse passes the rows of block I of pi_Q
+  const int iq = kLoc ? seg0 + Ib * kBlock + 32 * half + lq
+                      : min(max(pq[32 * half + lq], 0), a.N - 1);
+  const uint16_t* qh = a.q + bh * a.N * kHeadDim;
+  const uint16_t* kbase = a.k + (size_t)bg * a.N * kHeadDim;
+  const uint16_t* vbase = a.v + (size_t)bg * a.N * kHeadDim;
   const StoreAddr sta = store_addr(rg, lane);
   const ReadAddr ra = read_addr(lane);
-  auto first_key = [&](int s) -> int {
-    if (kLoc || s < ndiag_sparse || ntl == 0) return seg0 + s * kBlock + rg;
-    const int k = min(s - ndiag_sparse, max(ntl - 1, 0));
-    return Lt[(size_t)k * kBlock + rg];
-  };
-  const Staged r0 = load_rows(kbase, vbase, first_key(0), a.N, lane);
-  const Staged r1 = load_rows(kbase, vbase, first_key(1), a.N, lane);
-  Staged nxt = load_rows(kbase, vbase, first_key(2), a.N, lane);
-  int raw = kLoc ? 0 : first_key(3);
+  const Staged r0 = load_rows(kbase, vbase, key0, a.N, lane);
+  const Staged r1 = load_rows(kbase, vbase, key1, a.N, lane);
+  Staged nxt = load_rows(kbase, vbase, key2, a.N, lane);
 
   // the lane's query row as Q^T B operands, for the whole run
   bf16x8 qr[8];

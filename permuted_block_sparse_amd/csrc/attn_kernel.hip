@@ -424,15 +424,16 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_fwd(AttnArgs a) {
   // The first three tiles' rows are requested before the step count is
   // known (that takes a barrier): the local pass's tiles are the segment's
   // first key blocks, a sparse pass's the first tiles of L_t (indices
-  // clamped into a non-empty L_t; a workgroup of the first segment has no
-  // sparse tile and reads pi_Q instead). Rows of steps beyond the count are
-  // loaded and never used. The index loads go out with the block-order load, as
-  // neither depends on the other, and the row loads before the loads that
-  // wait for the block's rows: three dependent memory round trips before
-  // the first tile (block order, pi_Q, query rows; indices, key rows) where
-  // a plain order of the statements makes seven.
+  // clamped into L_t; in the first segment, which has no L_t and no sparse
+  // tile, an entry of pi_Q stands in as an in-bounds address). Rows of
+  // steps beyond the count are loaded and never used. The index loads go
+  // out with the block-order load, as neither depends on the other, and
+  // branch-free, so that no wait for one sits between them; the row loads
+  // go out before the wait for the block's pi_Q entries. That makes three
+  // dependent memory round trips before the first tile (block order, pi_Q
+  // entries, query rows; indices, key rows) where the plain order of the
+  // statements made seven.
   const int rg = gather_row(wave, lane);
-  // (branch-free, so that no wait for an index load sits between them)
   auto first_key = [&](int s) -> int {
     const bool computed = kLoc || s < ndiag_sparse || ntl == 0;
     const int k = min(max(s - ndiag_sparse, 0), max(ntl - 1, 0));

@@ -219,8 +219,7 @@ def main():
     visited = diag_tiles + sparse_tiles
     flop_launch = visited * TILE_FLOP
     achieved = flop_launch / (attn_mean * 1e-3) / 1e12
-    sel_pairs = B * Hq * T * S * (S + 1) / 2 + 4096.0 * sparse_tiles
-    pair_sparsity = 1.0 - sel_pairs / (B * Hq * N * (N + 1) / 2)
+    sel_stats = selection_stats(n_I, N, S, pl.pi_q())
     dense_flop = 4.0 * d * N * (N + 1) / 2 * B * Hq
 
     result = {
@@ -246,7 +245,8 @@ def main():
                       "overhead_frac": round(plan_ms / attn_med, 4),
                       "plan_then_prefill_one_stream": round(seq_ms, 4),
                       "step_fused": round(ms_step, 4)},
-        "stop": {"pair_sparsity": round(pair_sparsity, 5),
+        "stop": {"pair_sparsity": round(sel_stats["pair_sparsity"], 5),
+                 "tile_density": round(sel_stats["tile_density"], 5),
                  "mean_n_I": round(float(n_I.mean()), 2),
                  "visited_sparse_tiles": sparse_tiles,
                  "visited_local_tiles": diag_tiles,
@@ -282,6 +282,36 @@ def main():
         result["cpu_baseline"] = cpu_baseline(cfg, q, k, v, S, tau,
                                               nb_total=B * Hq * nb)
     print(json.dumps(result), flush=True)
+
+
+def selection_stats(n_I, N, S, pi_q=None):
+    """Pair sparsity and tile density of a selection (S2O page, Key points:
+    sparsity is the share of causal query-key pairs skipped, density its
+    complement; the tile density counts the 64 x 64 tiles a selection
+    touches, for performance accounting).
+
+    n_I: [B, Hq, N / 64], the tiles of L_t each query block attends;
+    pi_q: [B, Hq, N], the query order (needed for the tile density's local
+    tiles; None: no tile density). A row of segment t sees the keys of its
+    own segment up to itself (S (S + 1) / 2 pairs per segment and head) and
+    the 64 keys of each of its block's tiles (64 rows: 4096 pairs a tile).
+    A block touches local block c of its segment when its largest row
+    reaches the block's first key, i.e. blocks 0 .. (max row - t S) // 64.
+    """
+    n_I = np.asarray(n_I)
+    B, Hq, nb = n_I.shape
+    T = N // S
+    far = float(n_I.sum())
+    sel = B * Hq * T * S * (S + 1) / 2 + 4096.0 * far
+    out = {"pair_sparsity": 1.0 - sel / (B * Hq * N * (N + 1) / 2),
+           "visited_sparse_tiles": int(far)}
+    if pi_q is not None:
+        top = np.asarray(pi_q).reshape(B, Hq, nb, 64).max(axis=-1)
+        seg0 = (np.arange(nb) * 64) // S * S
+        local = int(((top - seg0) // 64 + 1).sum())
+        out["tile_density"] = (local + far) / (B * Hq * nb * (nb + 1) / 2)
+        out["local_tiles_touched"] = local
+    return out
 
 
 def scan_tiles_read(n_I, B, Hq, Hkv, N, S, chunk=32):
@@ -378,6 +408,7 @@ def extras(args, cfg, q, k, v, tq, tk, tv, pl, out, S, tau, timed):
     spec = cfg.spec
     B, Hq, Hkv, N = spec.batch, spec.heads_q, spec.heads_kv, spec.seq_len
     T = N // S
+    pi_q = pl.pi_q()
     res = {}
     # dense reference: the same kernel with tau = 0 visits every tile
     pl.set_tau(0.0)
@@ -400,15 +431,15 @@ def extras(args, cfg, q, k, v, tq, tk, tv, pl, out, S, tau, timed):
         pl.set_tau(t_)
         o_t = torch.empty_like(tq)
         ms, _ = timed(lambda: pbs.prefill(pl, tq, tk, tv, out=o_t), 3)
-        n_I = pl.n_I()
-        sel = B * Hq * T * S * (S + 1) / 2 + 4096.0 * n_I.sum()
-        sp = 1.0 - sel / (B * Hq * N * (N + 1) / 2)
+        st = selection_stats(pl.n_I(), N, S, pi_q)
+        sp = st["pair_sparsity"]
         diff = (o_t.float() - dense.float())
         mse = float((diff * diff).mean().item())
         per_head = (diff * diff).mean(dim=(0, 2, 3)).cpu().numpy()
         _, lse_t = pbs.prefill(pl, tq, tk, tv, out=o_t, return_lse=True)
         sweep.append({"tau": t_, "prefill_ms": round(ms, 4),
                       "pair_sparsity": round(float(sp), 5),
+                      "tile_density": round(st["tile_density"], 5),
                       "mse_vs_dense": mse,
                       "mse_per_head_max": float(per_head.max()),
                       "speedup_vs_dense": round(dense_ms / ms, 3),
@@ -427,10 +458,11 @@ def extras(args, cfg, q, k, v, tq, tk, tv, pl, out, S, tau, timed):
     loc_ms, _ = timed(lambda: pbs.prefill(pl_loc, tq, tk, tv, out=o_loc), 3)
     _, lse_loc = pbs.prefill(pl_loc, tq, tk, tv, out=o_loc, return_lse=True)
     diff = (o_loc.float() - dense.float())
-    sel = B * Hq * T * S * (S + 1) / 2
+    st = selection_stats(pl_loc.n_I(), N, S, pi_q)
     res["local_window_only"] = {
         "prefill_ms": round(loc_ms, 4),
-        "pair_sparsity": round(1.0 - sel / (B * Hq * N * (N + 1) / 2), 5),
+        "pair_sparsity": round(st["pair_sparsity"], 5),
+        "tile_density": round(st["tile_density"], 5),
         "mse_vs_dense": float((diff * diff).mean().item()),
         **recall_stats(lse_loc)}
     log(f"[bench] local window only: {res['local_window_only']}")
@@ -457,14 +489,14 @@ def extras(args, cfg, q, k, v, tq, tk, tv, pl, out, S, tau, timed):
     _, lse_b = pbs.prefill(pl, tq, tk, tv, out=o_b, return_lse=True)
     n_b = pl.n_I()
     pl.set_budget(-1)
-    sel = B * Hq * T * S * (S + 1) / 2 + 4096.0 * n_b.sum()
+    st = selection_stats(n_b, N, S, pi_q)
     diff = (o_b.float() - dense.float())
     res["fixed_budget_matched"] = {
         "budget_tiles": K, "visited_tiles": int(n_b.sum()),
         "tau_visited_tiles": visited_tau,
         "prefill_ms": round(b_ms, 4),
-        "pair_sparsity": round(float(1.0 - sel / (B * Hq * N * (N + 1) / 2)),
-                               5),
+        "pair_sparsity": round(st["pair_sparsity"], 5),
+        "tile_density": round(st["tile_density"], 5),
         "mse_vs_dense": float((diff * diff).mean().item()),
         **recall_stats(lse_b)}
     log(f"[bench] fixed budget (matched): {res['fixed_budget_matched']}")
@@ -494,15 +526,15 @@ def extras(args, cfg, q, k, v, tq, tk, tv, pl, out, S, tau, timed):
     _, lse_x = pbs.prefill(pl, tq, tk, tv, out=o_x, return_lse=True)
     n_x = pl.n_I()
     pl.set_max_threshold(float("nan"))
-    sel = B * Hq * T * S * (S + 1) / 2 + 4096.0 * n_x.sum()
+    st = selection_stats(n_x, N, S, pi_q)
     diff = (o_x.float() - dense.float())
     res["exact_max_matched"] = {
         "theta": round(lo_t, 5), "attended_tiles": int(n_x.sum()),
         "scored_tiles": int(sum(B * Hq * bps * t * bps for t in range(T))),
         "tau_visited_tiles": visited_tau,
         "prefill_ms": round(x_ms, 4),
-        "pair_sparsity": round(float(1.0 - sel / (B * Hq * N * (N + 1) / 2)),
-                               5),
+        "pair_sparsity": round(st["pair_sparsity"], 5),
+        "tile_density": round(st["tile_density"], 5),
         "mse_vs_dense": float((diff * diff).mean().item()),
         **recall_stats(lse_x)}
     log(f"[bench] exact max test (matched): {res['exact_max_matched']}")
@@ -516,13 +548,13 @@ def extras(args, cfg, q, k, v, tq, tk, tv, pl, out, S, tau, timed):
     seg_ms, _ = timed(lambda: pbs.prefill(pl_seg, tq, tk, tv, out=o_seg), 3)
     _, lse_seg = pbs.prefill(pl_seg, tq, tk, tv, out=o_seg, return_lse=True)
     n_seg = pl_seg.n_I()
-    sel = B * Hq * T * S * (S + 1) / 2 + 4096.0 * n_seg.sum()
+    st = selection_stats(n_seg, N, S, pl_seg.pi_q())
     diff = (o_seg.float() - dense.float())
     res["segment_kv_order"] = {
         "tau": tau, "plan_ms": round(plan_seg_ms, 4),
         "prefill_ms": round(seg_ms, 4),
-        "pair_sparsity": round(float(1.0 - sel / (B * Hq * N * (N + 1) / 2)),
-                               5),
+        "pair_sparsity": round(st["pair_sparsity"], 5),
+        "tile_density": round(st["tile_density"], 5),
         "mse_vs_dense": float((diff * diff).mean().item()),
         **recall_stats(lse_seg)}
     log(f"[bench] segment-local KV order: {res['segment_kv_order']}")

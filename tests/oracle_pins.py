@@ -12,6 +12,7 @@ answers, library routines, and invariants stated on the pages.
 """
 from __future__ import annotations
 
+import dataclasses
 import math
 from fractions import Fraction
 
@@ -597,6 +598,104 @@ def check_exact_max(O):
     assert (hi <= n_I).all() and hi.sum() < n_I.sum()
 
 
+# ------------------------------------------------------------------ metrics
+
+def check_selected_counts_bruteforce(O):
+    """|Sel(i)| of every row against an explicitly built key set (own-segment
+    keys j <= i plus the keys of the first n_I tiles of L_t, collected row
+    by row with the block of each row looked up in pi_Q), on a plan whose
+    query order is not the identity and with stop points that differ from
+    block to block."""
+    q, k, _ = _stripe(Hq=2, Hkv=1, N=384, d=16, seed=10)
+    S = 128
+    pl = O.plan(q, k, S)
+    n_I, _ = O.stop_points(q, k, pl, 0.3)
+    assert len(set(n_I[0, :, 2:].ravel().tolist())) > 1
+    assert not np.array_equal(pl.pi_q[0, 0], np.arange(384))
+    cnt = O.selected_counts(pl, n_I)
+    for h in range(2):
+        block_of_row = np.empty(384, dtype=np.int64)
+        block_of_row[pl.pi_q[0, h]] = np.arange(384) // 64
+        for i in range(384):
+            t = i // S
+            sel = set(range(t * S, i + 1))
+            n = int(n_I[0, h, block_of_row[i]])
+            if t > 0:
+                order = [int(j) for j in pl.pi_k[0, 0] if j < t * S]
+                sel |= set(order[:64 * n])
+            assert cnt[0, h, i] == len(sel), (h, i)
+
+
+def check_metrics_closed_forms(O):
+    """Pair sparsity (S2O page, Key points: the share of causal query-key
+    pairs skipped) in closed forms: 0 when nothing is skipped (tau = 0, or a
+    single segment at any tau); 1 - T S (S + 1) / (N (N + 1)) for the dense
+    local window only (each row sees the keys of its own segment up to
+    itself). Tile density: exactly 1 at tau = 0 with the identity query
+    order (block i of a segment touches local blocks 0..i, and all t S / 64
+    tiles of L_t); with constant keys (identity orders) it is
+    (sum of (i + 1) over the blocks + sum of n_I) over nb (nb + 1) / 2 with
+    n_I from the constant-key closed form. MSE: the mean of the squared
+    differences, against torch's mse_loss."""
+    q, k, v = _stripe(B=2, Hq=2, Hkv=1, N=512, d=32, seed=15)
+    N, S = 512, 128
+    T, nb = N // S, N // 64
+    for flags in (0, O.SA_NO_QPERM):
+        pl = O.plan(q, k, S, flags=flags)
+        n0, _ = O.stop_points(q, k, pl, 0.0)
+        m = O.metrics(pl, n0)
+        assert m["pair_sparsity"] == 0.0
+        if flags:
+            assert m["tile_density"] == 1.0
+        else:
+            assert m["tile_density"] > 1.0     # permuted blocks spread out
+    one = O.plan(q, k, N)
+    n1, _ = O.stop_points(q, k, one, 0.4)
+    assert O.metrics(one, n1)["pair_sparsity"] == 0.0
+    pll = O.plan(q, k, S, flags=O.SA_LOCAL_ONLY)
+    nl, _ = O.stop_points(q, k, pll, 0.0)
+    want = 1.0 - T * S * (S + 1) / (N * (N + 1))
+    assert abs(O.metrics(pll, nl)["pair_sparsity"] - want) < 1e-15
+    # constant keys: identity orders, n_I in closed form
+    rng = _rng(16)
+    d = 32
+    qc = bits(rng.standard_normal((1, 1, N, d)))
+    kc = np.broadcast_to(bits(rng.standard_normal(d)), (1, 1, N, d)).copy()
+    plc = O.plan(qc, kc, S)
+    tau = 0.05
+    nc, _ = O.stop_points(qc, kc, plc, tau)
+    visited = 0
+    pairs = 0
+    for I in range(nb):
+        t = I * 64 // S
+        i_loc = (I * 64 - t * S) // 64
+        D = sum(i - t * S + 1 for i in range(64 * I, 64 * I + 64))
+        n = 0 if t == 0 else _closed_form_n(tau, D, t, S)
+        visited += i_loc + 1 + n
+        pairs += D + 4096 * n
+    mc = O.metrics(plc, nc)
+    assert abs(mc["tile_density"] - visited / (nb * (nb + 1) / 2)) < 1e-15
+    assert abs(mc["pair_sparsity"] - (1 - pairs / (N * (N + 1) / 2))) < 1e-15
+    assert mc["visited_sparse_tiles"] == int(nc.sum())
+    # a hand-made query order of one segment of 128 rows: block 0 holds
+    # rows 1..64 (row 64 sees key 64, the first key of local block 1: one
+    # visible pair there), block 1 rows 0 and 65..127; each block touches
+    # both local blocks, so 4 of the nb (nb + 1) / 2 = 3 causal tiles
+    one2 = O.plan(q[:, :, :128], k[:, :, :128], 128)
+    pq = np.concatenate([np.arange(1, 65), [0], np.arange(65, 128)])
+    hand = dataclasses.replace(one2, pi_q=np.broadcast_to(
+        pq, one2.pi_q.shape).copy())
+    mh = O.metrics(hand, np.zeros((2, 2, 2), dtype=np.int64))
+    assert mh["tile_density"] == 4 / 3 and mh["pair_sparsity"] == 0.0
+    # MSE
+    o = rng.standard_normal((2, 2, 8, 4))
+    od = rng.standard_normal((2, 2, 8, 4))
+    mse = O.metrics(pl, n0, o, od)["mse"]
+    ref = torch.nn.functional.mse_loss(torch.from_numpy(o),
+                                       torch.from_numpy(od)).item()
+    assert abs(mse - ref) < 1e-15
+
+
 ALL_CHECKS = [
     check_fixed_point, check_dense_vs_sdpa, check_dense_closed_forms,
     check_worked_orders, check_stripe_score_bruteforce, check_plan_invariants,
@@ -606,5 +705,6 @@ ALL_CHECKS = [
     check_two_level_closed_form, check_permuted_block_closed_form,
     check_monotone_tau, check_local_only, check_recall,
     check_segment_kv_worked, check_segment_kv_invariants, check_budget,
-    check_exact_max,
+    check_exact_max, check_selected_counts_bruteforce,
+    check_metrics_closed_forms,
 ]

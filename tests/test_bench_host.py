@@ -105,3 +105,26 @@ def test_plan_bytes_streaming_passes_read_each_operand_once():
     for name in ("k_pool_q", "k_query_score", "k_block_qsum"):
         assert q_bytes <= res[name]["bytes"] < 1.1 * q_bytes, name
     assert k_bytes <= res["k_key_score"]["bytes"] < 1.2 * k_bytes
+
+
+def test_selection_stats_match_the_oracle_metrics():
+    # the bench's pair sparsity and tile density (from n_I and pi_Q alone)
+    # against the oracle's definitions (explicit per-row selected sets and
+    # per-block local tiles), on plans with a permuted and an identity
+    # query order, stop points that differ per block, and two batches
+    spec = StripeSpec(2, 4, 2, 1024, 128, n_vert=4, n_horiz=2, window=32,
+                      seed=5)
+    q, k, _ = make_stripe_inputs(spec)
+    S = 256
+    for flags, tau in ((0, 0.05), (0, 0.0), (O.SA_NO_QPERM, 0.2),
+                       (O.SA_LOCAL_ONLY, 0.0)):
+        pl = O.plan(q, k, S, flags=flags)
+        n_I, _ = O.stop_points(q, k, pl, tau)
+        want = O.metrics(pl, n_I)
+        got = bench.selection_stats(n_I, 1024, S, pl.pi_q)
+        assert abs(got["pair_sparsity"] - want["pair_sparsity"]) < 1e-12
+        assert abs(got["tile_density"] - want["tile_density"]) < 1e-12
+        assert got["visited_sparse_tiles"] == want["visited_sparse_tiles"]
+        assert got["local_tiles_touched"] == want["visited_diag_tiles"]
+        if tau == 0.05:
+            assert 0.0 < got["pair_sparsity"] < 1.0

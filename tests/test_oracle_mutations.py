@@ -14,6 +14,22 @@ SRC = pathlib.Path(S2O.__file__).read_text()
 
 # (name, exact text in oracle/s2o.py, replacement)
 MUTANTS = [
+    ("sel_local_off_by_one", "local = i - (i // S) * S + 1",
+     "local = i - (i // S) * S"),
+    ("sel_far_natural_order", "far[pl.pi_q[b, h]] = per_row * BLOCK",
+     "far[:] = per_row * BLOCK"),
+    ("sel_far_one_key_per_tile", "far[pl.pi_q[b, h]] = per_row * BLOCK",
+     "far[pl.pi_q[b, h]] = per_row"),
+    ("density_denominator_x2", "/ (B * Hq * nb * (nb + 1) / 2),",
+     "/ (B * Hq * nb * (nb + 1)),"),
+    ("density_diag_strict", "diag_tiles += int((rows.max(axis=1) >= j0).sum())",
+     "diag_tiles += int((rows.max(axis=1) > j0).sum())"),
+    ("density_diag_first_row", "diag_tiles += int((rows.max(axis=1) >= j0).sum())",
+     "diag_tiles += int((rows[:, 0] >= j0).sum())"),
+    ("sparsity_pairs_n2", "total_pairs = B * Hq * N * (N + 1) / 2",
+     "total_pairs = B * Hq * N * N / 2"),
+    ("mse_abs", "out[\"mse\"] = float(np.mean((o - o_dense) ** 2))",
+     "out[\"mse\"] = float(np.mean(np.abs(o - o_dense)))"),
     ("exact_mean_not_max", "mx = z.reshape(BLOCK, -1, BLOCK).max(axis=(0, 2))",
      "mx = z.reshape(BLOCK, -1, BLOCK).mean(axis=(0, 2))"),
     ("exact_strict", "sel = mx >= theta", "sel = mx > theta"),

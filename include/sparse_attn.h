@@ -160,10 +160,14 @@ int sparse_attn_plan(const sa_params* p, const void* q, const void* k,
  *   - each output row is written to its original position in O.
  * kappa = 1/sqrt(head_dim). q, k must be the tensors the plan was built
  * from (not checked: the stop points, and the plan's bound on the key norms
- * that keeps the softmax's exponentials finite, come from them). o: device
- * [batch, heads_q, seq_len, 128] bfloat16,
- * fully overwritten. lse (may be NULL): device [batch, heads_q, seq_len]
- * float32, natural-log log-sum-exp of kappa q.k over each row's key set.
+ * that keeps the softmax's exponentials finite, come from them). v: the
+ * value products run in fp16 (weights rounded to fp16, V converted into
+ * the workspace, exactly for entries of magnitude in [2^-14, 65504]);
+ * entries beyond 65504 in magnitude give unspecified results. o: device
+ * [batch, heads_q, seq_len, 128] bfloat16, fully overwritten (each value
+ * rounded to bfloat16 once, from fp32). lse (may be NULL): device
+ * [batch, heads_q, seq_len] float32, natural-log log-sum-exp of kappa q.k
+ * over each row's key set.
  * The stop points come from the plan (export N_I). After a setter below or
  * sparse_attn_plan_set_kv_order changed what they depend on, this call
  * first rescans them on `stream` (one extra launch), then launches the

@@ -291,11 +291,6 @@ def block_means(k64: np.ndarray, keys: np.ndarray) -> np.ndarray:
     return k64[keys].reshape(len(keys) // BLOCK, BLOCK, -1).mean(axis=1)
 
 
-def n_visible(rows: np.ndarray, j0: int) -> int:
-    """Number of (row, key) pairs with key j0 + c <= row, c in 0..63."""
-    return int(np.clip(rows - j0 + 1, 0, BLOCK).sum())
-
-
 def block_stop(qbar: np.ndarray, rows: np.ndarray, t: int,
                local_means: np.ndarray, tile_means: Optional[np.ndarray],
                S: int, tau: float, kap: float):
@@ -325,22 +320,25 @@ def block_stop(qbar: np.ndarray, rows: np.ndarray, t: int,
     """
     if t == 0:
         return 0, np.zeros(0)
-    # dense local window estimate, blocks in ascending order
+    # dense local window estimate, blocks in ascending order; nv[c] = number
+    # of (row, key) pairs of the block with key j0 + c' <= row, c' in 0..63
+    j0 = t * S + BLOCK * np.arange(S // BLOCK)
+    nv = np.clip(rows[None, :] - j0[:, None] + 1, 0, BLOCK).sum(axis=1)
+    s_loc = kap * (local_means @ qbar)
     acc = 0.0
     for c in range(S // BLOCK):
-        nv = n_visible(rows, t * S + c * BLOCK)
-        if nv > 0:
-            acc += (nv / BLOCK) * math.exp(kap * float(qbar @ local_means[c]))
+        if nv[c] > 0:
+            acc += (nv[c] / BLOCK) * math.exp(s_loc[c])
     # estimates past the stop point are computed but never used
     E = BLOCK * np.exp(kap * (tile_means @ qbar))
-    ps = []
-    for kk in range(len(tile_means)):
-        p = E[kk] / (acc + E[kk])
-        ps.append(p)
-        if p < tau:
-            return kk, np.asarray(ps)
-        acc += E[kk]
-    return len(tile_means), np.asarray(ps)
+    # running total before tile k: E_diag + E_0 + ... + E_{k-1}, added in
+    # that order (a cumulative sum adds left to right)
+    run = np.cumsum(np.concatenate(([acc], E)))[:-1]
+    ps = E / (run + E)
+    below = np.flatnonzero(ps < tau)
+    if len(below):
+        return int(below[0]), ps[:below[0] + 1]
+    return len(tile_means), ps
 
 
 def stop_points(q_bits, k_bits, pl: Plan, tau: float,
@@ -387,17 +385,21 @@ def stop_points(q_bits, k_bits, pl: Plan, tau: float,
     by_group: Dict[Tuple[int, int, int], list] = {}
     for b, h, I in blocks:
         by_group.setdefault((b, h // G, (I * BLOCK) // S), []).append((h, I))
-    q_cache: Dict[Tuple[int, int], np.ndarray] = {}
+    # decoded inputs of the current (b, KV head) only (groups are visited
+    # in (b, g, t) order)
+    cache: Dict[Tuple[int, int], tuple] = {}
     for (b, g, t), items in sorted(by_group.items()):
-        k64 = decode_bf16(k_bits[b, g])
+        if (b, g) not in cache:
+            cache.clear()
+            cache[(b, g)] = (decode_bf16(k_bits[b, g]), {})
+        k64, q_heads = cache[(b, g)]
         local_means = block_means(k64, np.arange(t * S, (t + 1) * S))
         tile_means = (block_means(k64, restricted_list(pl, b, g, t))
                       if t > 0 else None)
         for h, I in items:
-            if (b, h) not in q_cache:
-                q_cache.clear()
-                q_cache[(b, h)] = decode_bf16(q_bits[b, h])
-            q64 = q_cache[(b, h)]
+            if h not in q_heads:
+                q_heads[h] = decode_bf16(q_bits[b, h])
+            q64 = q_heads[h]
             rows = pl.pi_q[b, h, I * BLOCK:(I + 1) * BLOCK]
             qbar = q64[rows].mean(axis=0)
             n, ps = block_stop(qbar, rows, t, local_means, tile_means, S,

@@ -37,9 +37,23 @@ _EXPORT_DTYPES = {
 }
 
 
+def _stream_of(stream: Optional[torch.cuda.Stream]) -> torch.cuda.Stream:
+    return stream if stream is not None else torch.cuda.current_stream()
+
+
 def _stream_ptr(stream: Optional[torch.cuda.Stream]) -> int:
-    s = stream if stream is not None else torch.cuda.current_stream()
-    return s.cuda_stream
+    return _stream_of(stream).cuda_stream
+
+
+def _record(tensors, streams) -> None:
+    """Tell torch's caching allocator that work enqueued on `streams` uses
+    `tensors`: memory freed on the host side is not handed out again before
+    that work has completed (the library's kernels run on the caller's
+    streams, not necessarily torch's current one)."""
+    for s in streams:
+        for t in tensors:
+            if t is not None:
+                t.record_stream(s)
 
 
 def _check_tensor(x: torch.Tensor, name: str, heads_dim_ok=True):
@@ -95,8 +109,15 @@ class SparsePlan:
                 ctypes.c_size_t(nbytes), ctypes.c_void_p(_stream_ptr(stream)),
                 ctypes.byref(self._handle))
             _lib.check(st, "sparse_attn_plan")
+            self.used_on(stream)
         else:  # a call that builds the plan itself (sparse_attn_forward)
             _launch(self, nbytes)
+
+    def used_on(self, *streams) -> None:
+        """Record the workspace (and the inputs the plan points to) on the
+        streams whose enqueued work uses them."""
+        _record((self.workspace,) + self._inputs,
+                [_stream_of(s) for s in streams])
 
     @property
     def tau(self) -> float:
@@ -133,6 +154,8 @@ class SparsePlan:
             ctypes.c_void_p(_stream_ptr(stream))),
             "sparse_attn_plan_set_kv_order")
         self._keepalive = pi_k
+        self.used_on(stream)
+        _record((pi_k,), [_stream_of(stream)])
 
     def export(self, what: int, stream=None) -> np.ndarray:
         lib = _lib.load()
@@ -220,6 +243,8 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, segment: int,
            if return_lse else None)
     main = _stream_ptr(stream)
     side = _stream_ptr(side_stream) if side_stream is not None else main
+    streams = [_stream_of(stream)] + (
+        [side_stream] if side_stream is not None else [])
 
     def launch(pl, nbytes):
         st = lib.sparse_attn_forward(
@@ -231,6 +256,8 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, segment: int,
             ctypes.c_void_p(main), ctypes.c_void_p(side),
             ctypes.byref(pl._handle))
         _lib.check(st, "sparse_attn_forward")
+        pl.used_on(*streams)
+        _record((v, o, lse), streams)
 
     pl = SparsePlan(q, k, segment, tau, block, flags, stream, _launch=launch)
     return (pl, o, lse) if return_lse else (pl, o)
@@ -256,4 +283,6 @@ def prefill(pl: SparsePlan, q: torch.Tensor, k: torch.Tensor,
         ctypes.c_void_p(lse.data_ptr() if lse is not None else 0),
         ctypes.c_void_p(_stream_ptr(stream)))
     _lib.check(st, "sparse_attn_prefill")
+    pl.used_on(stream)
+    _record((q, k, v, o, lse), [_stream_of(stream)])
     return (o, lse) if return_lse else o

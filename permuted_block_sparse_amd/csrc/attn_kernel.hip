@@ -10,12 +10,15 @@
 // Two passes of one kernel per prefill. The local pass computes each query
 // block's dense local window in the rows' own order: block i of segment t
 // (rows t S + 64 i ..) against key blocks 0 .. i of the segment, only the
-// last one masked. It writes the normalised result to O and the
-// log2-sum-exp of each row to a scratch array. The sparse pass takes the
-// blocks of pi_Q: each row resumes from that state (reference = the local
-// log2-sum-exp, l = 1, accumulator = the local output) and continues over
-// the first n_I tiles of L_t, then overwrites its row of O. The softmax
-// does not depend on the order in which a row's keys are visited. A block
+// last one masked. It writes the normalised result to O (bf16), its
+// residual below that bf16 value to a scratch array (bf16; the two carry
+// about 16 significant bits of the fp32 result) and the log2-sum-exp of
+// each row. The sparse pass takes the blocks of pi_Q: each row resumes from
+// that state (reference = the local log2-sum-exp, l = 1, accumulator = the
+// local output, the bf16 value plus its residual) and continues over the
+// first n_I tiles of L_t, then overwrites its row of O, so the output is
+// rounded to bf16 once. The softmax does not depend on the order in which
+// a row's keys are visited. A block
 // of pi_Q holds rows from all over its segment, so in that order its local
 // window would need every key block of the segment with about half of the
 // pairs masked; in the rows' own order it needs about half as many tiles.
@@ -60,8 +63,11 @@
 //                   lane's tile sum instead (a sum above 2^8 divides the row
 //                   by its largest p); workgroups with other rows take the
 //                   row maximum of every tile (a further launch);
-//   O^T += V^T P^T: V^T A operands via ds_read_tr16_b64 transposed reads,
-//                   P^T B operands straight from the S registers.
+//   O^T += V^T P^T: fp16 products (P rounded to fp16, 2^-11 relative, and
+//                   V read from an fp16 copy, exact for bf16 values of
+//                   magnitude in [2^-14, 65504]); V^T A operands via
+//                   ds_read_tr16_b64 transposed reads, P^T B operands
+//                   straight from the S registers.
 //
 // LDS layouts follow the MFMA operand reads: each read instruction of a wave
 // touches one 1 KB (K, ds_read_b128) or 512 B (V, ds_read_tr16_b64) block,
@@ -99,6 +105,9 @@ constexpr float kSafeSpan = 120.0f;
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mfma32(f16x8 a, f16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 
 // Cross-lane exchanges without LDS round trips: DPP within rows of 16,
@@ -292,9 +301,9 @@ __device__ __forceinline__ void pv_tile(const char* Vt, const f32x16 (&sacc)[2],
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
     const int kb = s >> 1, half = s & 1;
-    bf16x8 pb;
+    f16x8 pb;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) pb[e] = (__bf16)sacc[kb][8 * half + e];
+    for (int e = 0; e < 8; ++e) pb[e] = (_Float16)sacc[kb][8 * half + e];
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
       const int id = ((2 * kb + half) * 4 + db) * 2;
@@ -302,7 +311,7 @@ __device__ __forceinline__ void pv_tile(const char* Vt, const f32x16 (&sacc)[2],
       const s16x4 lo = lds_read_tr16(p);
       const s16x4 hi = lds_read_tr16(p + 512);
       const s16x8 cat = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-      oacc[db] = mfma32(__builtin_bit_cast(bf16x8, cat), pb, oacc[db]);
+      oacc[db] = mfma32(__builtin_bit_cast(f16x8, cat), pb, oacc[db]);
     }
   }
 }
@@ -450,7 +459,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_fwd(AttnArgs a) {
   const size_t bh = (size_t)b * a.Hq + h;
   const int32_t* pq = a.pi_q + bh * a.N + (size_t)I * kBlock;
   int32_t* nI_ptr = a.n_I + bh * (a.N / kBlock) + I;
-  const int nI_raw = *nI_ptr;  // unconditional: no wait for it until used
+  // sparse passes: unconditional, no wait for it until used; the local pass
+  // reads nothing the planner writes (it may run beside the planner)
+  const int nI_raw = kLoc ? 0 : *nI_ptr;
   const int nI = (!valid || kLoc) ? 0 : kExact ? ntl : min(max(nI_raw, 0), ntl);
   // my row: the local pass takes the segment's rows in their own order,
   // the sparse passes the rows of block I of pi_Q
@@ -473,26 +484,31 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_fwd(AttnArgs a) {
                                              16 * s + 8 * lh);
 
   // The local pass starts from nothing; the sparse passes continue the
-  // online softmax of the local pass, whose normalised output (bf16, in O)
-  // and log2-sum-exp are the state o = acc / l, l = 1 for reference m =
-  // log2-sum-exp.
+  // online softmax of the local pass, whose normalised output (the bf16
+  // value in O plus its bf16 residual) and log2-sum-exp are the state
+  // o = acc / l, l = 1 for reference m = log2-sum-exp.
   f32x16 oacc[4];
   float m = -INFINITY, l = 0.f;
   if (kLoc) {
 #pragma unroll
     for (int db = 0; db < 4; ++db) oacc[db] = f32x16{};
   } else {
-    const uint16_t* orow0 = a.o + (bh * a.N + iq) * kHeadDim;
+    const size_t ro = (bh * a.N + iq) * kHeadDim;
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
-        const uint2 w = *reinterpret_cast<const uint2*>(
-            orow0 + db * 32 + 8 * g4 + 4 * lh);
-        oacc[db][4 * g4 + 0] = __uint_as_float(w.x << 16);
-        oacc[db][4 * g4 + 1] = __uint_as_float(w.x & 0xffff0000u);
-        oacc[db][4 * g4 + 2] = __uint_as_float(w.y << 16);
-        oacc[db][4 * g4 + 3] = __uint_as_float(w.y & 0xffff0000u);
+        const size_t e = ro + db * 32 + 8 * g4 + 4 * lh;
+        const uint2 w = *reinterpret_cast<const uint2*>(a.o + e);
+        const uint2 r = *reinterpret_cast<const uint2*>(a.olo + e);
+        oacc[db][4 * g4 + 0] =
+            __uint_as_float(w.x << 16) + __uint_as_float(r.x << 16);
+        oacc[db][4 * g4 + 1] = __uint_as_float(w.x & 0xffff0000u) +
+                               __uint_as_float(r.x & 0xffff0000u);
+        oacc[db][4 * g4 + 2] =
+            __uint_as_float(w.y << 16) + __uint_as_float(r.y << 16);
+        oacc[db][4 * g4 + 3] = __uint_as_float(w.y & 0xffff0000u) +
+                               __uint_as_float(r.y & 0xffff0000u);
       }
     m = a.lse2[bh * a.N + iq];
     l = 1.f;
@@ -521,9 +537,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_fwd(AttnArgs a) {
     return;
   }
 
-  // Tile indices: every step loads the index of the row this lane gathers
-  // three steps later (local steps load a harmless in-bounds value and
-  // compute their indices instead).
+  // Tile indices: step s of a sparse pass loads the index of the row this
+  // lane fetches for tile s + 4 (steps past the last one load a harmless
+  // in-bounds value); the local pass computes its indices.
   auto key_src = [&](int s, int row) -> const int32_t* {
     return (s >= ndiag && s < nsteps) ? Lt + (size_t)(s - ndiag) * kBlock + row
                                       : pq + (row & 63);
@@ -639,7 +655,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_fwd(AttnArgs a) {
     char* const nb = tiles[(s + 2) % 3];
     store_rows(nb, nb + kTileBytes, nxt, sta);
     nxt = stage(s + 3, raw);
-    raw = *key_src(s + 4, rg);
+    if (!kLoc) raw = *key_src(s + 4, rg);
     wait_lgkm0();
     __builtin_amdgcn_s_barrier();
   };
@@ -651,20 +667,29 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_fwd(AttnArgs a) {
   if (s < nsteps) body(s, sa, sb);
   __builtin_amdgcn_s_waitcnt(0);  // index loads of steps never taken
 
-  // ---- epilogue: normalise, round to bf16, scatter to the original rows.
+  // ---- epilogue: normalise, round to bf16, scatter to the original rows
+  // (the local pass also stores each value's residual below its bf16 value,
+  // for the sparse pass to resume from).
   if (!valid) return;
   const float ln2 = 0.69314718055994530942f;
   const float inv = 1.f / l;
-  uint16_t* orow = a.o + (bh * a.N + iq) * kHeadDim;
+  const size_t ro = (bh * a.N + iq) * kHeadDim;
 #pragma unroll
   for (int db = 0; db < 4; ++db)
 #pragma unroll
     for (int g4 = 0; g4 < 4; ++g4) {
       const int d0 = db * 32 + 8 * g4 + 4 * lh;
-      __bf16 v4[4];
+      __bf16 v4[4], r4[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) v4[j] = (__bf16)(oacc[db][4 * g4 + j] * inv);
-      *reinterpret_cast<uint2*>(orow + d0) = __builtin_bit_cast(uint2, v4);
+      for (int j = 0; j < 4; ++j) {
+        const float y = oacc[db][4 * g4 + j] * inv;
+        v4[j] = (__bf16)y;
+        if (kLoc) r4[j] = (__bf16)(y - (float)v4[j]);  // exact difference
+      }
+      *reinterpret_cast<uint2*>(a.o + ro + d0) = __builtin_bit_cast(uint2, v4);
+      if (kLoc)
+        *reinterpret_cast<uint2*>(a.olo + ro + d0) =
+            __builtin_bit_cast(uint2, r4);
     }
   const float lse2v = m + log2f(l);
   if (kLoc && lh == 0) a.lse2[bh * a.N + iq] = lse2v;
@@ -672,9 +697,39 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_fwd(AttnArgs a) {
   if (kExact && lane == 0 && half == 0) *nI_ptr = n_visit;
 }
 
+// V in fp16 for the PV products: each bf16 value (8 bits of significand) is
+// exactly an fp16 value when its magnitude lies in fp16's normal range
+// [2^-14, 65504]; smaller ones round to fp16's subnormal steps of 2^-24,
+// larger ones overflow. One thread per 8 values (16-byte loads and stores).
+__global__ __launch_bounds__(256) void k_v_to_f16(const uint4* __restrict__ v,
+                                                  uint4* __restrict__ v16,
+                                                  long long n8) {
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n8) return;
+  const uint4 w = v[i];
+  const uint32_t in[4] = {w.x, w.y, w.z, w.w};
+  uint32_t out[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    h2 r;
+    r[0] = (_Float16)__uint_as_float(in[j] << 16);
+    r[1] = (_Float16)__uint_as_float(in[j] & 0xffff0000u);
+    out[j] = __builtin_bit_cast(uint32_t, r);
+  }
+  v16[i] = make_uint4(out[0], out[1], out[2], out[3]);
+}
+
 int attention_blocks_per_wg() { return 4; }
 
 hipError_t launch_attention_local(const AttnArgs& a, hipStream_t s) {
+  const long long n8 = (long long)a.B * a.Hkv * a.N * (kHeadDim / 8);
+  hipLaunchKernelGGL(k_v_to_f16, dim3((unsigned)((n8 + 255) / 256)),
+                     dim3(256), 0, s,
+                     reinterpret_cast<const uint4*>(a.v_in),
+                     reinterpret_cast<uint4*>(a.v16), n8);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   const int total = a.n_groups * a.wg_per_group;
   // the dense local windows in the rows' own order
   hipLaunchKernelGGL(k_attn_fwd<kLocal>, dim3(total), dim3(kThreads), 0, s, a);

@@ -75,7 +75,7 @@ struct StopArgs {
   long long list_len;
   int B, Hq, Hkv, N, S, T, G;
   double tau;
-  float c2;         // kappa * log2(e)
+  double c2;        // kappa * log2(e)
   int fixed;        // >= 0: n_I = min(fixed, t S / 64), no scan
 };
 hipError_t launch_stop_scan(const StopArgs& a, hipStream_t s);
@@ -90,7 +90,9 @@ hipError_t launch_block_order(const PlanDims& d, const int32_t* n_I,
 struct AttnArgs {
   const uint16_t* q;
   const uint16_t* k;
-  const uint16_t* v;
+  const uint16_t* v;      // V as fp16, the copy the PV products read
+  const uint16_t* v_in;   // the caller's V (bf16), converted into v
+  uint16_t* v16;          // = v, writable (the conversion's output)
   uint16_t* o;
   float* lse;
   const int32_t* pi_q;
@@ -104,15 +106,17 @@ struct AttnArgs {
   const float* kmax2;  // per (b, KV head): the largest |k_j|^2 (fp32)
   int32_t* wg_flag;    // per workgroup: 1 = logits unbounded (kMaxRef runs it)
   float* lse2;         // per row: the local pass's log2-sum-exp (exp2 domain)
+  uint16_t* olo;       // per row: the local output's residual below its bf16
+                       // value in O ([B, Hq, N, 128] bf16)
   int local_only;      // 1: the local pass only (no sparse tile visited)
   int local_steps;     // local steps of the sparse passes: always 0
   const int32_t* border;  // per group: blocks by stop point (null: in order)
   int exact;       // 1: exact per-block max test instead of the stop points
   float exact_thr; // that test's threshold on the raw dot products (theta / kappa)
 };
-// The local pass (every row's dense local window, rows in their own order;
-// needs nothing from the plan but its workspace) and the sparse passes
-// (after the local pass and the stop points).
+// The local pass (V converted to fp16, then every row's dense local window,
+// rows in their own order; needs nothing from the plan but its workspace)
+// and the sparse passes (after the local pass and the stop points).
 hipError_t launch_attention_local(const AttnArgs& a, hipStream_t s);
 hipError_t launch_attention_sparse(const AttnArgs& a, hipStream_t s);
 // Query blocks one attention workgroup processes (sets wg_per_group).

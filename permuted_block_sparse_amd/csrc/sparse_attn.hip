@@ -25,7 +25,7 @@ struct Layout {
   size_t pool_part, pooled, vscore, blocksum, segsum, contrast, u;
   size_t key_a, idx_a, key_b, idx_b;
   size_t pi_k, L, pi_q, n_I, rcnt, rcum, qsum, kpart, kmax2, wg_flag, lse2,
-      border;
+      border, olo, v16;
   size_t total;
 };
 
@@ -109,6 +109,8 @@ Layout layout_of(const PlanDims& d) {
   L.wg_flag = take(attention_workgroups(d) * sizeof(int32_t));
   L.lse2 = take(nbh * d.N * sizeof(float));
   L.border = take(nbh * (d.N / kBlock) * sizeof(int32_t));
+  L.olo = take(nbh * d.N * kHeadDim * sizeof(uint16_t));
+  L.v16 = take(nbg * d.N * kHeadDim * sizeof(uint16_t));
   L.total = off;
   return L;
 }
@@ -217,7 +219,7 @@ int run_stop_scan(const sa_plan* pl, hipStream_t s) {
   a.T = d.T;
   a.G = d.G;
   a.tau = pl->p.tau;
-  a.c2 = (float)(1.4426950408889634074 / std::sqrt((double)kHeadDim));
+  a.c2 = 1.4426950408889634074 / std::sqrt((double)kHeadDim);
   if (pl->p.flags & SA_LOCAL_ONLY)
     a.fixed = 0;
   else if (pl->budget >= 0)
@@ -323,7 +325,9 @@ AttnArgs attn_args(const sa_plan* plan, const void* q, const void* k,
   AttnArgs a;
   a.q = static_cast<const uint16_t*>(q);
   a.k = static_cast<const uint16_t*>(k);
-  a.v = static_cast<const uint16_t*>(v);
+  a.v_in = static_cast<const uint16_t*>(v);
+  a.v16 = plan->at<uint16_t>(plan->lay.v16);
+  a.v = a.v16;
   a.o = static_cast<uint16_t*>(o);
   a.lse = lse;
   a.pi_q = plan->at<int32_t>(plan->lay.pi_q);
@@ -351,6 +355,7 @@ AttnArgs attn_args(const sa_plan* plan, const void* q, const void* k,
   a.kmax2 = plan->at<float>(plan->lay.kmax2);
   a.wg_flag = plan->at<int32_t>(plan->lay.wg_flag);
   a.lse2 = plan->at<float>(plan->lay.lse2);
+  a.olo = plan->at<uint16_t>(plan->lay.olo);
   a.local_only = (plan->p.flags & SA_LOCAL_ONLY) ? 1 : 0;
   a.local_steps = 0;
   a.border = (!a.exact && block_order_used(d))

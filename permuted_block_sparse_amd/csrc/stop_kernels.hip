@@ -21,9 +21,14 @@
 //                  test in float64; stops once every block has stopped.
 //
 // Arithmetic (shared with nothing else): a tile's mean logit is
-// (qsum . ksum) * kappa / 4096 with both sums in fp32 over bf16 inputs,
-// exponentiated in fp32 (exp2), then the estimate, running total and share
-// test in float64 as est < tau * (acc + est).
+// (qsum . ksum) * kappa / 4096 with both sums in fp32 over bf16 inputs and
+// their dot product summed in float64 (products rounded to fp32). The share E_k / (Acc + E_k) does not depend
+// on a common factor of the estimates, so every estimate is taken relative
+// to a running reference, the largest mean logit seen so far (the running
+// total is rescaled when it rises): exp2 of a non-positive argument in fp32,
+// never overflowing and never 0 for the largest term, whatever the scale of
+// the logits. The running total and the share test are in float64, the test
+// as est < tau * (acc + est).
 
 #include "sa_device.h"
 #include "sa_launch.h"
@@ -84,6 +89,24 @@ static __device__ __forceinline__ float quad_sum(float x) {
                                                0xF, true));  // [1,0,3,2]
   x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF,
                                                0xF, true));  // [2,3,0,1]
+  return x;
+}
+static __device__ __forceinline__ double quad_sum_f64(double x) {
+  auto dpp = [](double v, int ctrl) {
+    const uint64_t u = __double_as_longlong(v);
+    int lo = (int)(uint32_t)u, hi = (int)(uint32_t)(u >> 32);
+    if (ctrl == 0xB1) {
+      lo = __builtin_amdgcn_mov_dpp(lo, 0xB1, 0xF, 0xF, true);
+      hi = __builtin_amdgcn_mov_dpp(hi, 0xB1, 0xF, 0xF, true);
+    } else {
+      lo = __builtin_amdgcn_mov_dpp(lo, 0x4E, 0xF, 0xF, true);
+      hi = __builtin_amdgcn_mov_dpp(hi, 0x4E, 0xF, 0xF, true);
+    }
+    return __longlong_as_double(
+        (long long)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo));
+  };
+  x += dpp(x, 0xB1);  // [1,0,3,2]
+  x += dpp(x, 0x4E);  // [2,3,0,1]
   return x;
 }
 static __device__ __forceinline__ int quad_sum_int(int x) {
@@ -162,7 +185,7 @@ __global__ __launch_bounds__(kScanThreads) void k_stop_scan(StopArgs a) {
   const uint16_t* kbase = a.k + (long long)bg * a.N * kHeadDim;
   const int32_t* Lt = a.L + (long long)bg * a.list_len +
                       (long long)a.S * t * (t - 1) / 2;
-  const float c2k = a.c2 / (float)(kBlock * kBlock);
+  const double c2k = (double)a.c2 / (double)(kBlock * kBlock);
 
   // key sums of tiles first .. first + 31 of a sequence into LDS; wave w
   // takes tiles w, w + 8, w + 16, w + 24
@@ -182,20 +205,33 @@ __global__ __launch_bounds__(kScanThreads) void k_stop_scan(StopArgs a) {
       }
     }
   };
-  // this quad's mean-logit exponent of tile kk in LDS: exp2 of
-  // (qsum . ksum) kappa log2(e) / 4096, fp32
-  auto tile_exp = [&](int kk) {
+  // this quad's mean logit of tile kk in LDS, in log2 units:
+  // (qsum . ksum) kappa log2(e) / 4096; each product rounded once to fp32,
+  // the sum of the 128 products in float64 (its error does not grow with
+  // the partial sums, whatever the size of the logits)
+  auto tile_x = [&](int kk) {
     const float4* src = reinterpret_cast<const float4*>(&ksum[kk][32 * dq]);
-    float d = 0.f;
+    double d = 0.0;
 #pragma unroll
     for (int x = 0; x < 8; ++x) {
       const float4 f = src[x];
-      d = fmaf(qv[4 * x], f.x, d);
-      d = fmaf(qv[4 * x + 1], f.y, d);
-      d = fmaf(qv[4 * x + 2], f.z, d);
-      d = fmaf(qv[4 * x + 3], f.w, d);
+      d += (double)(qv[4 * x] * f.x);
+      d += (double)(qv[4 * x + 1] * f.y);
+      d += (double)(qv[4 * x + 2] * f.z);
+      d += (double)(qv[4 * x + 3] * f.w);
     }
-    return __builtin_amdgcn_exp2f(quad_sum(d) * c2k);
+    return quad_sum_f64(d) * c2k;
+  };
+  // estimates relative to the running reference ref (the largest mean
+  // logit so far): exp2(x - ref) after raising ref to x if needed, with the
+  // running total acc (relative to ref as well) rescaled then
+  double ref = -INFINITY;
+  auto rel_exp = [&](double x, double& acc) {
+    if (x > ref) {
+      acc *= (double)__builtin_amdgcn_exp2f((float)(ref - x));  // 0 at first
+      ref = x;
+    }
+    return (double)__builtin_amdgcn_exp2f((float)(x - ref));
   };
 
   // dense local window: E_diag = sum over the segment's 64-key blocks c, in
@@ -218,8 +254,11 @@ __global__ __launch_bounds__(kScanThreads) void k_stop_scan(StopArgs a) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) nv += min(max(rofs[i] - j0 + 1, 0), kBlock);
         nv = quad_sum_int(nv);
-        const float ex = tile_exp(kk);
-        if (nv > 0) acc += ((double)nv / kBlock) * (double)ex;
+        const double x = tile_x(kk);
+        if (nv > 0) {
+          const double ex = rel_exp(x, acc);
+          acc += ((double)nv / kBlock) * ex;
+        }
       }
     }
   }
@@ -234,7 +273,7 @@ __global__ __launch_bounds__(kScanThreads) void k_stop_scan(StopArgs a) {
     __syncthreads();
     if (active) {
       for (int kk = 0; kk < cnt; ++kk) {
-        const double est = kBlock * (double)tile_exp(kk);
+        const double est = kBlock * rel_exp(tile_x(kk), acc);
         if (est < a.tau * (acc + est)) {
           n = k0 + kk;
           active = false;

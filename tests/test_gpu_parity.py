@@ -382,10 +382,12 @@ def test_parity_llama_layer_n32k_full_plan_sampled_outputs():
     say(f"   sampled blocks: max_abs={err:.3g} mse={mse:.3g}")
 
 
-def _sampled_check(q, k, v, S, tau, flags, pl, label, n_blocks=24, seed=11):
+def _sampled_check(q, k, v, S, tau, flags, pl, label, n_blocks=24, seed=11,
+                   all_stops=False):
     """One GPU run at full size against the oracle: every index array
-    bit-exact, then stop points and outputs of sampled query blocks (plus
-    the first and last block of the last head)."""
+    bit-exact, then stop points (of every block with all_stops, else of the
+    sampled ones) and outputs of sampled query blocks (plus the first and
+    last block of the last head)."""
     g = run_gpu(q, k, v, S, tau, flags)
     assert_plan_equal(g, pl)
     B, Hq, N = q.shape[:3]
@@ -395,7 +397,11 @@ def _sampled_check(q, k, v, S, tau, flags, pl, label, n_blocks=24, seed=11):
         rng.integers(0, B, n_blocks), rng.integers(0, Hq, n_blocks),
         rng.integers(0, nb, n_blocks))]
     blocks += [(B - 1, Hq - 1, nb - 1), (0, 0, 0)]
-    n_orc, traces = O.stop_points(q, k, pl, tau, blocks=blocks)
+    if all_stops:
+        say(f"   {label}: oracle stop points of all {B * Hq * nb} blocks")
+        n_orc, traces = O.stop_points(q, k, pl, tau)
+    else:
+        n_orc, traces = O.stop_points(q, k, pl, tau, blocks=blocks)
     mask = n_orc >= 0
     gn = np.where(mask, g["n_I"], -1)
     ties = stop_mismatches(gn, n_orc, traces, tau)
@@ -404,46 +410,214 @@ def _sampled_check(q, k, v, S, tau, flags, pl, label, n_blocks=24, seed=11):
         n_use[b, h, I] = g["n_I"][b, h, I]
     o_ref, lse_ref = O.attend(q, k, v, pl, n_use, blocks=blocks)
     err, mse = assert_outputs_close(g["o"], o_ref, g["lse"], lse_ref)
-    say(f"   {label}: ties={len(ties)} mean_n_I={g['n_I'].mean():.2f} "
-        f"sampled max_abs={err:.3g} mse={mse:.3g}")
+    say(f"   {label}: stop points compared {int(mask.sum())} ties={len(ties)}"
+        f" mean_n_I={g['n_I'].mean():.2f} sampled max_abs={err:.3g} "
+        f"mse={mse:.3g}")
     return g
 
 
-@pytest.mark.parametrize("cid", [3, 4, 5])
-def test_parity_full_size_sampled(cid):
-    """The 128K Llama-shaped layer (every tau of its sweep), the 128K
-    Qwen-shaped layer (every segment length) and the batch-4 64K layer
-    (S2O, KV permutation only, tau = 0 against dense attention) at their
-    full sizes in the launch configuration the benchmark times: index arrays
-    bit-exact, stop points and outputs of sampled blocks."""
+_INPUTS = {}
+
+
+def _inputs(cid):
+    """The workload's inputs, generated once per workload for the tests of
+    this module that use it (the previous workload's are dropped)."""
+    if cid not in _INPUTS:
+        _INPUTS.clear()
+        _INPUTS[cid] = make_stripe_inputs(get_config(cid).spec)
+    return _INPUTS[cid]
+
+
+def _full_runs():
+    runs = []
+    c3, c4, c5 = get_config(3), get_config(4), get_config(5)
+    runs += [(3, c3.segment, t_, 0, t_ == c3.tau) for t_ in c3.taus]
+    runs += [(4, S_, c4.tau, 0, S_ == 1024) for S_ in c4.segments]
+    runs += [(5, c5.segment, c5.tau, 0, False),
+             (5, c5.segment, c5.tau, O.SA_NO_QPERM, False)]
+    return runs
+
+
+@pytest.mark.parametrize("cid,S,tau,flags,all_stops", _full_runs(),
+                         ids=[f"cfg{r[0]}-S{r[1]}-tau{r[2]}-flags{r[3]}"
+                              for r in _full_runs()])
+def test_parity_full_size(cid, S, tau, flags, all_stops):
+    """The 128K Llama-shaped layer (every tau of its sweep; every stop point
+    at tau = 0.005), the 128K Qwen-shaped layer (every segment length; every
+    stop point at S = 1024) and the batch-4 64K layer (S2O and KV
+    permutation only) at their full sizes in the launch configuration the
+    benchmark times: index arrays bit-exact, stop points and outputs of
+    sampled blocks."""
     cfg = get_config(cid)
     say(f"[full] workload {cfg.name}: inputs")
-    q, k, v = make_stripe_inputs(cfg.spec)
-    runs = []
-    if cid == 3:
-        runs = [(cfg.segment, t_, 0) for t_ in cfg.taus]
-    elif cid == 4:
-        runs = [(S_, cfg.tau, 0) for S_ in cfg.segments]
-    else:
-        runs = [(cfg.segment, cfg.tau, 0),
-                (cfg.segment, cfg.tau, O.SA_NO_QPERM)]
-    plans = {}
-    for S, tau, flags in runs:
-        key = (S, flags)
-        if key not in plans:
-            say(f"[full] oracle plan S={S} flags={flags}")
-            plans[key] = O.plan(q, k, S, flags=flags)
-        say(f"[full] GPU S={S} tau={tau} flags={flags}")
-        _sampled_check(q, k, v, S, tau, flags, plans[key],
-                       f"S={S} tau={tau} flags={flags}")
-    if cid == 5:
-        say("[full] tau = 0 against dense attention on sampled rows")
-        g = run_gpu(q, k, v, cfg.segment, 0.0)
-        rng = np.random.default_rng(3)
-        N = q.shape[2]
-        rows = rng.integers(0, N, 12)
-        for b, h in [(0, 0), (3, 31), (2, 17)]:
-            od, ld = O.dense_causal(q, k, v, rows=rows, heads=[(b, h)])
-            err = np.abs(g["o"][b, h, rows] - od[b, h, rows]).max()
-            assert err <= 2e-2, err
-            assert np.abs(g["lse"][b, h, rows] - ld[b, h, rows]).max() <= 2e-3
+    q, k, v = _inputs(cid)
+    say(f"[full] oracle plan S={S} flags={flags}")
+    pl = O.plan(q, k, S, flags=flags)
+    say(f"[full] GPU S={S} tau={tau} flags={flags}")
+    _sampled_check(q, k, v, S, tau, flags, pl,
+                   f"S={S} tau={tau} flags={flags}", all_stops=all_stops)
+
+
+def test_parity_batch4_tau0_is_dense():
+    """The batch-4 64K layer at tau = 0 against dense causal attention
+    (float64 oracle) on sampled rows of three heads."""
+    cfg = get_config(5)
+    q, k, v = _inputs(5)
+    say("[full] tau = 0 against dense attention on sampled rows")
+    g = run_gpu(q, k, v, cfg.segment, 0.0)
+    rng = np.random.default_rng(3)
+    N = q.shape[2]
+    rows = rng.integers(0, N, 12)
+    for b, h in [(0, 0), (3, 31), (2, 17)]:
+        od, ld = O.dense_causal(q, k, v, rows=rows, heads=[(b, h)])
+        err = np.abs(g["o"][b, h, rows] - od[b, h, rows]).max()
+        assert err <= 2e-2, err
+        assert np.abs(g["lse"][b, h, rows] - ld[b, h, rows]).max() <= 2e-3
+
+
+def _bits(x):
+    return round_to_bf16_bits(np.asarray(x, dtype=np.float32))
+
+
+def test_local_heavy_outputs_in_4_8():
+    """Values in [4, 8) (bf16 step 2^-5) and attention whose local window
+    carries a large share of each row's mass (up to about a half): one
+    rounding of the final value to bf16 costs up to 2^-6 here, which leaves
+    little of the 2e-2 bound. The state the local pass hands to the sparse
+    pass must not be rounded to bf16 on the way (rounding it there and
+    again at the end reaches about 0.024), and the weights of the PV
+    products must be finer than bf16 (2^-9 relative of values up to 8 is
+    another 0.016 at worst; fp16 weights leave 0.002). Every row's query
+    and key share a random direction (a strong diagonal), scaled by a."""
+    rng = np.random.default_rng(44)
+    N, d, S, tau = 2048, 128, 512, 0.01
+    r = rng.standard_normal((N, d))
+    r /= np.linalg.norm(r, axis=1, keepdims=True)
+    worst = 0.0
+    for a in (5.0, 7.0):
+        q = _bits((a * r + 0.3 * rng.standard_normal((N, d)))[None, None])
+        k = _bits((a * r + 0.3 * rng.standard_normal((N, d)))[None, None])
+        v = _bits(np.minimum(4.0 + 4.0 * rng.random((1, 1, N, d)), 7.96875))
+        say(f"[local heavy] a={a}")
+        err, mse, nties, g, pl, n_orc = _check_case(q, k, v, S, tau, 0)
+        # the share of the local window in each row's mass (oracle)
+        pll = O.plan(q, k, S, flags=O.SA_LOCAL_ONLY)
+        nl, _ = O.stop_points(q, k, pll, 0.0)
+        _, l_loc = O.attend(q, k, v, pll, nl)
+        _, l_all = O.attend(q, k, v, pl, n_orc)
+        share = np.exp(l_loc - l_all)[0, 0, S:]
+        say(f"   max_abs={err:.4g} mse={mse:.3g} local share mean "
+            f"{share.mean():.3f} max {share.max():.3f}")
+        assert share.mean() > 0.15 and share.max() > 0.4
+        assert g["n_I"][0, 0, S // 64:].min() > 0
+        worst = max(worst, err)
+    say(f"   worst max_abs {worst:.4g} (one bf16 rounding in [4, 8): "
+        f"{0.5 * 2.0 ** -5:.4g})")
+
+
+def test_saturated_fixed_point_and_wide_pooled_query():
+    """Inputs whose fixed-point images saturate (entries of magnitude >= 128
+    map to -32768 / 32767) in queries and keys, with G N = 131072 query rows
+    per KV head: the pooled query then has entries beyond +-2^32, so the key
+    scores' int64 arithmetic on the GPU uses the high word of every factor.
+    Logits stay moderate: the saturated query dimensions meet key entries
+    of at most 8 / 256, the saturated key entries meet query entries of at
+    most 4 / 256."""
+    rng = np.random.default_rng(45)
+    B, Hq, Hkv, N, d, S = 1, 8, 1, 16384, 128, 2048
+    spec = _spec(B, Hq, Hkv, N, 46, n_vert=32, window=128)
+    q, k, v = make_stripe_inputs(spec)
+    qf = bf16_bits_to_float32(q).astype(np.float64)
+    kf = bf16_bits_to_float32(k).astype(np.float64)
+    qf[..., 0] = 200.0
+    qf[..., 1] = -300.0
+    qf[..., 2] = rng.integers(-4, 5, size=qf[..., 2].shape) / 256.0
+    kf[..., 0] = rng.integers(-8, 9, size=kf[..., 0].shape) / 256.0
+    kf[..., 1] = rng.integers(-8, 9, size=kf[..., 1].shape) / 256.0
+    kf[..., 2] = 0.0
+    hot = rng.choice(N, 64, replace=False)
+    kf[0, 0, hot, 2] = rng.choice([-250.0, -130.0, 128.0, 255.0], size=64)
+    q, k = _bits(qf), _bits(kf)
+    fq = O.fixed_point(q)
+    assert (fq[..., 0] == 32767).all() and (fq[..., 1] == -32768).all()
+    assert (np.abs(O.fixed_point(k[0, 0, hot, 2])) >= 32767).all()
+    pl = O.plan(q, k, S)
+    assert np.abs(pl.pooled).max() >= 2 ** 32
+    assert (pl.pooled[0, 0, :2] == [32767 * Hq * N, -32768 * Hq * N]).all()
+    for tau in (0.005, 0.05):
+        say(f"[saturated] tau={tau}")
+        err, mse, nties, g, _, _ = _check_case(q, k, v, S, tau, 0)
+        say(f"   max_abs={err:.3g} mse={mse:.3g} ties={nties} "
+            f"mean_n_I={g['n_I'].mean():.2f}")
+
+
+def test_stop_points_with_large_mean_logits():
+    """Mean-pooled logits between about 75 and 180 (natural log units):
+    exp of them overflows fp32 above about 88.7, but the running share of
+    the stop rule does not depend on a common factor of the estimates, so
+    the stop points must still match the oracle's (float64) ones. Queries
+    and keys share one direction u, keys with one weight per 64 keys."""
+    rng = np.random.default_rng(47)
+    N, d, S = 4096, 128, 512
+    u = rng.standard_normal(d)
+    u /= np.linalg.norm(u)
+    qf = 34.0 * u + rng.standard_normal((1, 2, N, d))
+    w = np.repeat(rng.uniform(25.0, 60.0, size=N // 64), 64).reshape(
+        1, 1, N, 1)
+    kf = w * u + rng.standard_normal((1, 1, N, d))
+    q, k = _bits(qf), _bits(kf)
+    v = _bits(rng.standard_normal((1, 1, N, d)))
+    qm = bf16_bits_to_float32(q).astype(np.float64).mean(axis=2)
+    km = bf16_bits_to_float32(k).astype(np.float64)
+    tm = km[0, 0].reshape(-1, 64, d).mean(axis=1)
+    ml = (tm @ qm[0].T) / np.sqrt(d)
+    say(f"[large logits] tile mean logits {ml.min():.1f} .. {ml.max():.1f}")
+    assert ml.min() > 60.0 and ml.max() > 150.0
+    for tau in (0.001, 0.01, 0.1):
+        say(f"[large logits] tau={tau}")
+        err, mse, nties, g, pl, n_orc = _check_case(q, k, v, S, tau, 0)
+        full = np.repeat(np.arange(N // S) * (S // 64), S // 64)
+        stopped = (g["n_I"][0] < full[None, :]).sum()
+        say(f"   max_abs={err:.3g} mse={mse:.3g} ties={nties} "
+            f"mean_n_I={g['n_I'].mean():.2f} blocks stopped early {stopped}")
+        if tau >= 0.01:
+            assert stopped > 0
+
+
+def test_non_current_streams():
+    """plan, prefill and forward on streams other than torch's current one
+    (the binding records its workspace, inputs and outputs on the streams
+    that use them) give the bits of the default path, also when the plan
+    objects are dropped right after their last launch and new tensors are
+    allocated on the current stream before anything has finished."""
+    import torch
+    import permuted_block_sparse_amd as pbs
+    from tests.gpu_helpers import to_device
+    spec = _spec(1, 4, 2, 4096, 48, n_vert=32, window=128)
+    q, k, v = make_stripe_inputs(spec)
+    tq, tk, tv = to_device(q), to_device(k), to_device(v)
+    S, tau = 512, 0.05
+    pl = pbs.plan(tq, tk, S, tau)
+    o_ref, l_ref = pbs.prefill(pl, tq, tk, tv, return_lse=True)
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    s1.wait_stream(torch.cuda.current_stream())
+    s2.wait_stream(torch.cuda.current_stream())
+    say("[streams] plan + prefill on a second stream")
+    p1 = pbs.plan(tq, tk, S, tau, stream=s1)
+    o1, l1 = pbs.prefill(p1, tq, tk, tv, return_lse=True, stream=s1)
+    del p1
+    junk = [torch.full((1 << 24,), 7, dtype=torch.int32, device="cuda:0")
+            for _ in range(4)]
+    say("[streams] forward on two other streams")
+    pf, of, lf = pbs.forward(tq, tk, tv, S, tau, return_lse=True, stream=s1,
+                             side_stream=s2)
+    del pf
+    junk += [torch.full((1 << 24,), 9, dtype=torch.int32, device="cuda:0")
+             for _ in range(4)]
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o_ref.view(torch.int16))
+    assert torch.equal(l1, l_ref)
+    assert torch.equal(of.view(torch.int16), o_ref.view(torch.int16))
+    assert torch.equal(lf, l_ref)
+    del junk

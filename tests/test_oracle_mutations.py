@@ -30,6 +30,12 @@ MUTANTS = [
      "total_pairs = B * Hq * N * N / 2"),
     ("mse_abs", "out[\"mse\"] = float(np.mean((o - o_dense) ** 2))",
      "out[\"mse\"] = float(np.mean(np.abs(o - o_dense)))"),
+    ("stop_after_next", "return int(below[0]), ps[:below[0] + 1]",
+     "return int(below[0]) + 1, ps[:below[0] + 1]"),
+    ("running_sum_from_zero", "run = np.cumsum(np.concatenate(([acc], E)))[:-1]",
+     "run = np.cumsum(np.concatenate(([0.0], E)))[:-1]"),
+    ("local_from_segment_start", "j0 = t * S + BLOCK * np.arange(S // BLOCK)",
+     "j0 = BLOCK * np.arange(S // BLOCK)"),
     ("exact_mean_not_max", "mx = z.reshape(BLOCK, -1, BLOCK).max(axis=(0, 2))",
      "mx = z.reshape(BLOCK, -1, BLOCK).mean(axis=(0, 2))"),
     ("exact_strict", "sel = mx >= theta", "sel = mx > theta"),
@@ -71,20 +77,23 @@ MUTANTS = [
      "top = kx[:BLOCK].sum(axis=0)"),
     ("restrict_le", "Lt = order[order < t * S]",
      "Lt = order[order <= t * S][:t * S]"),
-    ("stop_le", "if p < tau:", "if p <= tau:"),
-    ("diag_weight", "acc += (nv / BLOCK) * math.exp", "acc += nv * math.exp"),
+    ("stop_le", "below = np.flatnonzero(ps < tau)",
+     "below = np.flatnonzero(ps <= tau)"),
+    ("diag_weight", "acc += (nv[c] / BLOCK) * math.exp",
+     "acc += nv[c] * math.exp"),
     ("tile_mass_1", "E = BLOCK * np.exp(kap * (tile_means @ qbar))",
      "E = np.exp(kap * (tile_means @ qbar))"),
-    ("no_running_sum", "        acc += E[kk]\n", "\n"),
+    ("no_running_sum", "run = np.cumsum(np.concatenate(([acc], E)))[:-1]",
+     "run = np.full(len(E), acc)"),
     ("estimate_no_kappa", "E = BLOCK * np.exp(kap * (tile_means @ qbar))",
      "E = BLOCK * np.exp(tile_means @ qbar)"),
     ("local_means_shifted", "local_means = block_means(k64, np.arange(t * S, (t + 1) * S))",
      "local_means = block_means(k64, np.arange(t * S - S, t * S))"),
-    ("ratio_without_self", "p = E[kk] / (acc + E[kk])", "p = E[kk] / acc"),
+    ("ratio_without_self", "ps = E / (run + E)", "ps = E / run"),
     ("qbar_natural_rows", "qbar = q64[rows].mean(axis=0)",
      "qbar = q64[I * BLOCK:(I + 1) * BLOCK].mean(axis=0)"),
-    ("nvis_clip63", "np.clip(rows - j0 + 1, 0, BLOCK)",
-     "np.clip(rows - j0, 0, BLOCK)"),
+    ("nvis_clip63", "np.clip(rows[None, :] - j0[:, None] + 1, 0, BLOCK)",
+     "np.clip(rows[None, :] - j0[:, None], 0, BLOCK)"),
     ("dense_kappa_1_over_d", "return 1.0 / math.sqrt(d)", "return 1.0 / d"),
     ("dense_mask_ge", "z[np.arange(N)[None, :] > r[:, None]] = -np.inf",
      "z[np.arange(N)[None, :] >= r[:, None]] = -np.inf"),

@@ -29,7 +29,13 @@ Pinned parts (see tests/test_oracle_*.py):
     of the tile order, invariants, and tau = 0 reproducing dense attention;
   * the exact per-block maximum test -- tile maxima by brute force (library
     einsum), theta = -inf / +inf reproducing dense / local-only attention,
-    monotone selection in theta.
+    monotone selection in theta;
+  * the per-block centroid Top-K selection -- tile scores as sums of the
+    integer logit matrix with ranks counted pairwise, a hand-derived case in
+    which blocks of one segment choose different tiles (and ties), K = 0 /
+    K >= all reproducing local-only / dense attention;
+  * the metrics -- selected-set sizes against explicit per-row key sets,
+    closed forms of pair sparsity and tile density, MSE against torch.
 Parity unpinned: the agreement of the sparsity/MSE figures with the numbers
 printed on the S2O summary page (those need real models and datasets).
 """
@@ -37,12 +43,12 @@ from .s2o import (SA_NO_QPERM, SA_NO_KVPERM, SA_NO_EARLYSTOP, SA_LOCAL_ONLY,
                   SA_SEGMENT_KV,
                   Plan, decode_bf16, fixed_point, dense_causal, plan,
                   stop_points, attend, recall, exact_max_selection,
-                  s2o_attention,
+                  topk_selection, s2o_attention,
                   selected_counts, metrics, restricted_list, kappa_of)
 
 __all__ = ["SA_NO_QPERM", "SA_NO_KVPERM", "SA_NO_EARLYSTOP", "SA_LOCAL_ONLY",
            "SA_SEGMENT_KV",
            "Plan", "decode_bf16", "fixed_point", "dense_causal", "plan",
            "stop_points", "attend", "recall", "exact_max_selection",
-           "s2o_attention",
+           "topk_selection", "s2o_attention",
            "selected_counts", "metrics", "restricted_list", "kappa_of"]

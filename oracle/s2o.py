@@ -512,6 +512,68 @@ def exact_max_selection(q_bits, k_bits, pl: Plan, theta: float,
     return n_I, masks, maxima
 
 
+def topk_selection(q_bits, k_bits, pl: Plan, K: int,
+                            blocks: Optional[Sequence[Tuple[int, int, int]]]
+                            = None):
+    """Per-block Top-K tile selection from mean-pooled centroids, instead of
+    the tau stop: the AB-Sparse page's block-sparse workflow (the paragraph
+    around its Figure 2 and the footnote on mean pooling) scores every key
+    block by the product of the query with the block's centroid, the mean
+    of its keys, and attends the K best blocks. Here the query side is the
+    query block's mean query as well (one selection per 64-row block, as
+    the attention works on 64 x 64 tiles).
+
+    For query block I of segment t: every tile T_k of L_t gets the score
+    r_k = (sum of fx(q_i) over the block's 64 rows) . (sum of fx(k_j) over
+    the tile's 64 keys) -- 4096 times the block's mean query against the
+    tile's centroid, both in the fixed-point images of the orders; the
+    block attends to the min(K, t S / 64) tiles of highest r_k, ties by
+    smaller position in L_t. READING: the page ranks by real-valued
+    products; as for every order of this method, the ranking is done on
+    exact integers (fixed-point images, int64 sums) so that it is
+    reproducible bit for bit; the dense local window is always attended;
+    SA_LOCAL_ONLY still attends to no tile.
+    Returns (counts n_I [B, Hq, N/64], masks (b, h, I) -> bool per tile of
+    L_t, scores (b, h, I) -> int64 r per tile).
+    """
+    B, Hq, N, d = q_bits.shape
+    G = Hq // pl.heads_kv
+    S = pl.segment
+    nb = N // BLOCK
+    n_I = np.full((B, Hq, nb), -1, dtype=np.int64)
+    masks, scores = {}, {}
+    if blocks is None:
+        blocks = [(b, h, I) for b in range(B) for h in range(Hq)
+                  for I in range(nb)]
+    kx_cache: Dict[Tuple[int, int], np.ndarray] = {}
+    qx_cache: Dict[Tuple[int, int], np.ndarray] = {}
+    for b, h, I in blocks:
+        g = h // G
+        t = (I * BLOCK) // S
+        ntl = t * S // BLOCK
+        if t == 0 or pl.flags & SA_LOCAL_ONLY or K <= 0:
+            n_I[b, h, I] = 0
+            masks[(b, h, I)] = np.zeros(ntl, dtype=bool)
+            scores[(b, h, I)] = np.zeros(0, dtype=np.int64)
+            continue
+        if (b, g) not in kx_cache:
+            kx_cache[(b, g)] = fixed_point(k_bits[b, g])
+        if (b, h) not in qx_cache:
+            qx_cache[(b, h)] = fixed_point(q_bits[b, h])
+        rows = pl.pi_q[b, h, I * BLOCK:(I + 1) * BLOCK]
+        qs = qx_cache[(b, h)][rows].sum(axis=0)                  # int64 [d]
+        tiles = restricted_list(pl, b, g, t).reshape(-1, BLOCK)
+        ks = kx_cache[(b, g)][tiles].sum(axis=1)                 # int64 [ntl, d]
+        r = ks @ qs                                              # int64 [ntl]
+        order = np.lexsort((np.arange(ntl), -r))   # r desc, position asc
+        sel = np.zeros(ntl, dtype=bool)
+        sel[order[:min(K, ntl)]] = True
+        n_I[b, h, I] = int(sel.sum())
+        masks[(b, h, I)] = sel
+        scores[(b, h, I)] = r
+    return n_I, masks, scores
+
+
 def recall(q_bits, k_bits, pl: Plan, n_I: np.ndarray,
            blocks: Optional[Sequence[Tuple[int, int, int]]] = None):
     """Attention recall of each row: the share of its dense causal attention

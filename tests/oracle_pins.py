@@ -696,6 +696,97 @@ def check_metrics_closed_forms(O):
     assert abs(mse - ref) < 1e-15
 
 
+# ------------------------------------------------- centroid Top-K selection
+
+def check_topk_bruteforce(O):
+    """Per-block Top-K from mean-pooled centroids: each tile's score is the
+    sum of the block's 64 x 64 matrix of integer logits fx(q_i) . fx(k_j)
+    over its rows and the tile's keys (by bilinearity the pooled product);
+    the selection holds the tiles whose rank, counted pairwise on (score,
+    -position), is below K; n_I counts them."""
+    q, k, _ = _stripe(Hq=2, Hkv=1, N=512, d=16, seed=17)
+    S = 128
+    pl = O.plan(q, k, S)
+    qx = [O.fixed_point(q[0, h]) for h in range(2)]
+    kx = O.fixed_point(k[0, 0])
+    for K in (1, 3, 5):
+        n_I, masks, scores = O.topk_selection(q, k, pl, K)
+        for h in range(2):
+            for I in range(512 // 64):
+                t = I * 64 // S
+                ntl = t * S // 64
+                rows = pl.pi_q[0, h, 64 * I:64 * I + 64]
+                if t == 0:
+                    assert n_I[0, h, I] == 0 and not masks[(0, h, I)].any()
+                    continue
+                tiles = O.restricted_list(pl, 0, 0, t).reshape(-1, 64)
+                r = [int((qx[h][rows] @ kx[tiles[c]].T).sum())
+                     for c in range(ntl)]
+                assert [int(x) for x in scores[(0, h, I)]] == r
+                rank = [sum(1 for c2 in range(ntl)
+                            if (r[c2], -c2) > (r[c], -c)) for c in range(ntl)]
+                want = [rk < K for rk in rank]
+                assert masks[(0, h, I)].tolist() == want, (K, h, I)
+                assert n_I[0, h, I] == min(K, ntl)
+
+
+def check_topk_worked(O):
+    """Hand-derived selection (N = 384, S = 128, d = 8). Segment 0's queries
+    are e1 (coordinate 0 = 1), segment 1's rows 128..191 e2 and 192..255
+    e1, segment 2's rows zero; keys 0..63 are e1, keys 64..127 e2, the rest
+    zero. The pooled query is 256 (192 e1 + 64 e2), so the e1 keys rank
+    first: L_1 = [e1 tile, e2 tile], L_2 = [e1, e2, keys 128..191, keys
+    192..255]. C_1 = 2^20 (e1 - e2), so segment 1's order puts the e1
+    queries first: block 2 = rows 192..255, block 3 = rows 128..191.
+    K = 1: block 2 takes the e1 tile, block 3 the e2 tile (a fixed budget
+    would give both the e1 tile); segment 2's zero queries score every tile
+    0, so ties go to the first positions: K = 1 -> tile 0, K = 3 -> tiles
+    0..2; K = 9 -> every tile."""
+    N, d, S = 384, 8, 128
+    qf = np.zeros((1, 1, N, d))
+    qf[0, 0, :128, 0] = 1.0
+    qf[0, 0, 128:192, 1] = 1.0
+    qf[0, 0, 192:256, 0] = 1.0
+    kf = np.zeros((1, 1, N, d))
+    kf[0, 0, :64, 0] = 1.0
+    kf[0, 0, 64:128, 1] = 1.0
+    q, k = bits(qf), bits(kf)
+    pl = O.plan(q, k, S)
+    assert list(pl.pi_q[0, 0, 128:256]) == list(range(192, 256)) + list(
+        range(128, 192))
+    want = {1: {2: [1, 0], 3: [0, 1], 4: [1, 0, 0, 0], 5: [1, 0, 0, 0]},
+            3: {2: [1, 1], 3: [1, 1], 4: [1, 1, 1, 0], 5: [1, 1, 1, 0]},
+            9: {2: [1, 1], 3: [1, 1], 4: [1, 1, 1, 1], 5: [1, 1, 1, 1]}}
+    for K, per_block in want.items():
+        n_I, masks, _ = O.topk_selection(q, k, pl, K)
+        for I, m in per_block.items():
+            assert masks[(0, 0, I)].astype(int).tolist() == m, (K, I)
+            assert n_I[0, 0, I] == sum(m)
+        assert n_I[0, 0, 0] == n_I[0, 0, 1] == 0
+
+
+def check_topk_closed_forms(O):
+    """K = 0 attends the dense local window only (the SA_LOCAL_ONLY
+    outputs); K at least the number of tiles attends everything (dense
+    attention); SA_LOCAL_ONLY attends to no tile whatever K."""
+    q, k, v = _stripe(Hq=2, Hkv=1, N=512, d=32, seed=18)
+    S = 128
+    pl = O.plan(q, k, S)
+    n0, m0, _ = O.topk_selection(q, k, pl, 0)
+    o0, l0 = O.attend(q, k, v, pl, n0, tile_mask=m0)
+    pll = O.plan(q, k, S, flags=O.SA_LOCAL_ONLY)
+    nl, _ = O.stop_points(q, k, pll, 0.0)
+    ol, ll = O.attend(q, k, v, pll, nl)
+    assert (n0 == 0).all()
+    assert np.abs(o0 - ol).max() < 1e-12 and np.abs(l0 - ll).max() < 1e-12
+    na, ma, _ = O.topk_selection(q, k, pl, 512 // 64)
+    oa, la = O.attend(q, k, v, pl, na, tile_mask=ma)
+    od, ld = O.dense_causal(q, k, v)
+    assert np.abs(oa - od).max() < 1e-12 and np.abs(la - ld).max() < 1e-12
+    nL, mL, _ = O.topk_selection(q, k, pll, 3)
+    assert (nL == 0).all() and not any(m.any() for m in mL.values())
+
+
 ALL_CHECKS = [
     check_fixed_point, check_dense_vs_sdpa, check_dense_closed_forms,
     check_worked_orders, check_stripe_score_bruteforce, check_plan_invariants,
@@ -706,5 +797,6 @@ ALL_CHECKS = [
     check_monotone_tau, check_local_only, check_recall,
     check_segment_kv_worked, check_segment_kv_invariants, check_budget,
     check_exact_max, check_selected_counts_bruteforce,
-    check_metrics_closed_forms,
+    check_metrics_closed_forms, check_topk_bruteforce, check_topk_worked,
+    check_topk_closed_forms,
 ]

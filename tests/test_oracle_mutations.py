@@ -36,6 +36,18 @@ MUTANTS = [
      "run = np.cumsum(np.concatenate(([0.0], E)))[:-1]"),
     ("local_from_segment_start", "j0 = t * S + BLOCK * np.arange(S // BLOCK)",
      "j0 = BLOCK * np.arange(S // BLOCK)"),
+    ("topk_tie_desc", "order = np.lexsort((np.arange(ntl), -r))   # r desc, position asc",
+     "order = np.lexsort((-np.arange(ntl), -r))"),
+    ("topk_ascending", "order = np.lexsort((np.arange(ntl), -r))   # r desc, position asc",
+     "order = np.lexsort((np.arange(ntl), r))"),
+    ("topk_natural_rows", "qs = qx_cache[(b, h)][rows].sum(axis=0)",
+     "qs = qx_cache[(b, h)][I * BLOCK:(I + 1) * BLOCK].sum(axis=0)"),
+    ("topk_first_key", "ks = kx_cache[(b, g)][tiles].sum(axis=1)",
+     "ks = kx_cache[(b, g)][tiles[:, 0]]"),
+    ("topk_one_more", "sel[order[:min(K, ntl)]] = True",
+     "sel[order[:min(K + 1, ntl)]] = True"),
+    ("topk_global_order", "sel[order[:min(K, ntl)]] = True",
+     "sel[:min(K, ntl)] = True"),
     ("exact_mean_not_max", "mx = z.reshape(BLOCK, -1, BLOCK).max(axis=(0, 2))",
      "mx = z.reshape(BLOCK, -1, BLOCK).mean(axis=(0, 2))"),
     ("exact_strict", "sel = mx >= theta", "sel = mx > theta"),

@@ -220,6 +220,28 @@ int sparse_attn_plan_set_budget(sa_plan* plan, int32_t tiles);
  * tile. */
 int sparse_attn_plan_set_max_threshold(sa_plan* plan, double theta);
 
+/* Per-block Top-K tile selection from mean-pooled centroids instead of the
+ * tau stop (the AB-Sparse page's block-sparse workflow, the paragraph
+ * around its Figure 2 and the footnote on mean pooling: key blocks scored
+ * by the product of the query with their centroid, the best K attended).
+ * With tiles >= 0, every query block I of segment t >= 1 scores each tile
+ * T_k of L_t by r = (sum of fx(q) over I's 64 rows) . (sum of fx(k) over
+ * T_k's 64 keys) -- exact integers, fx as in sparse_attn_plan -- and
+ * attends to the min(tiles, t S / 64) tiles of highest r, ties by smaller
+ * position in L_t; the dense local window is always attended and n_I
+ * counts the selected tiles. The scoring (an fp64 MFMA contraction per
+ * segment, exact) and the selection are enqueued on `stream` by this call;
+ * `scratch` (device, 8-byte aligned, at least
+ * sparse_attn_topk_scratch_bytes(plan) bytes: one int64 per block and
+ * tile) is used only by that work. The selections stay with the plan until
+ * the next call of this function or of sparse_attn_plan_set_kv_order
+ * (which ends the mode). tiles < 0 restores the tau stop (scratch may then
+ * be NULL). The exact maximum test takes precedence; SA_LOCAL_ONLY still
+ * visits no tile. Returns SA_ERR_WORKSPACE_TOO_SMALL for a short scratch. */
+size_t sparse_attn_topk_scratch_bytes(const sa_plan* plan);
+int sparse_attn_plan_set_topk(sa_plan* plan, int32_t tiles, void* scratch,
+                              size_t scratch_bytes, hipStream_t stream);
+
 /* What sparse_attn_plan_export copies (element type, count). */
 #define SA_EXPORT_PI_K         0  /* int32 [B, Hkv, N]                        */
 #define SA_EXPORT_PI_Q         1  /* int32 [B, Hq, N]                         */
@@ -229,6 +251,9 @@ int sparse_attn_plan_set_max_threshold(sa_plan* plan, double theta);
 #define SA_EXPORT_QUERY_SCORE  5  /* int64 [B, Hq, N]: u                      */
 #define SA_EXPORT_CONTRAST     6  /* int64 [B, Hkv, T, 128]: C (t = 0 zero)   */
 #define SA_EXPORT_POOLED       7  /* int64 [B, Hkv, 128]: P                   */
+#define SA_EXPORT_TOPK_MASK    8  /* uint32 [B, Hq, N / 64, 64]: Top-K tiles  */
+                                  /* selected (bit p of word w: position    */
+                                  /* 32 w + p of L_t)                        */
 
 /* Bytes of one export (0 for an unknown `what`). */
 size_t sparse_attn_plan_export_bytes(const sa_plan* plan, int what);

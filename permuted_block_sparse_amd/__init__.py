@@ -34,6 +34,7 @@ _EXPORT_DTYPES = {
     _lib.SA_EXPORT_L: np.int32, _lib.SA_EXPORT_N_I: np.int32,
     _lib.SA_EXPORT_KEY_SCORE: np.int64, _lib.SA_EXPORT_QUERY_SCORE: np.int64,
     _lib.SA_EXPORT_CONTRAST: np.int64, _lib.SA_EXPORT_POOLED: np.int64,
+    _lib.SA_EXPORT_TOPK_MASK: np.uint32,
 }
 
 
@@ -141,6 +142,37 @@ class SparsePlan:
         logits instead of the tau stop (NaN: back to the tau stop)."""
         _lib.check(_lib.load().sparse_attn_plan_set_max_threshold(
             self._handle, float(theta)), "sparse_attn_plan_set_max_threshold")
+
+    def set_topk(self, tiles: int, stream=None) -> None:
+        """Per-block centroid Top-K selection of `tiles` tiles of L_t
+        instead of the tau stop (tiles < 0: back to the tau stop). The
+        scores' scratch is allocated here for the work this call enqueues
+        and released when it has run."""
+        lib = _lib.load()
+        if tiles < 0:
+            _lib.check(lib.sparse_attn_plan_set_topk(
+                self._handle, int(tiles), None, 0,
+                ctypes.c_void_p(_stream_ptr(stream))),
+                "sparse_attn_plan_set_topk")
+            return
+        n = int(lib.sparse_attn_topk_scratch_bytes(self._handle))
+        s = _stream_of(stream)
+        with torch.cuda.stream(s):
+            scratch = torch.empty(max(n, 8), dtype=torch.uint8,
+                                  device=self.workspace.device)
+        _lib.check(lib.sparse_attn_plan_set_topk(
+            self._handle, int(tiles), ctypes.c_void_p(scratch.data_ptr()),
+            ctypes.c_size_t(n), ctypes.c_void_p(s.cuda_stream)),
+            "sparse_attn_plan_set_topk")
+        self.used_on(stream)
+        _record((scratch,), [s])
+
+    def topk_masks(self):
+        """Selected tiles of every block after set_topk: uint32
+        [B, Hq, N / 64, 64], bit p of word w = position 32 w + p of L_t."""
+        B, Hq, N, _ = self.shape
+        return self.export(_lib.SA_EXPORT_TOPK_MASK).reshape(B, Hq, N // 64,
+                                                             64)
 
     def set_kv_order(self, pi_k: torch.Tensor, stream=None) -> None:
         if pi_k.dtype != torch.int32 or not pi_k.is_cuda:

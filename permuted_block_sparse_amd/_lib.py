@@ -29,12 +29,14 @@ SA_EXPORT_KEY_SCORE = 4
 SA_EXPORT_QUERY_SCORE = 5
 SA_EXPORT_CONTRAST = 6
 SA_EXPORT_POOLED = 7
+SA_EXPORT_TOPK_MASK = 8
 
 EXPORTED_SYMBOLS = (
     "sparse_attn_workspace_bytes", "sparse_attn_plan", "sparse_attn_prefill",
     "sparse_attn_forward",
     "sparse_attn_plan_set_tau", "sparse_attn_plan_set_budget",
     "sparse_attn_plan_set_max_threshold",
+    "sparse_attn_topk_scratch_bytes", "sparse_attn_plan_set_topk",
     "sparse_attn_plan_export_bytes",
     "sparse_attn_plan_export", "sparse_attn_plan_set_kv_order",
     "sparse_attn_plan_destroy", "sparse_attn_status_string",
@@ -86,6 +88,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.sparse_attn_plan_set_budget.restype = i32
     lib.sparse_attn_plan_set_max_threshold.argtypes = [vp, ctypes.c_double]
     lib.sparse_attn_plan_set_max_threshold.restype = i32
+    lib.sparse_attn_topk_scratch_bytes.argtypes = [vp]
+    lib.sparse_attn_topk_scratch_bytes.restype = sz
+    lib.sparse_attn_plan_set_topk.argtypes = [vp, i32, vp, sz, vp]
+    lib.sparse_attn_plan_set_topk.restype = i32
     lib.sparse_attn_plan_export_bytes.argtypes = [vp, i32]
     lib.sparse_attn_plan_export_bytes.restype = sz
     lib.sparse_attn_plan_export.argtypes = [vp, i32, vp, sz, vp]

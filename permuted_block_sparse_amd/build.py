@@ -11,8 +11,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "lib", "libsparse_attn.so")
 
-SOURCES = ["plan_kernels.hip", "stop_kernels.hip", "attn_kernel.hip",
-           "sparse_attn.hip"]
+SOURCES = ["plan_kernels.hip", "stop_kernels.hip", "topk_kernels.hip",
+           "attn_kernel.hip", "sparse_attn.hip"]
 
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

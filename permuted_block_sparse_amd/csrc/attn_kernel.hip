@@ -370,20 +370,38 @@ __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F
 // max test deciding every tile of L_t in the loop. Workgroups of the sparse
 // instances with no tile to visit exit at once: the local pass's output is
 // final for their rows.
-enum : int { kMaxRef = 0, kFastRef = 1, kExactMax = 2, kLocal = 3 };
+// kTopKMax and kTopKFast: the sparse pass over the per-block Top-K
+// selections (a bitmask over the positions of L_t per block): the workgroup
+// steps through the union of its blocks' selected positions, and a wave
+// whose block did not select a position runs that step as a no-op (both
+// halves of a block share a SIMD, so skipping the work would not shorten
+// the step, which waits for the busiest SIMD); the two reference paths as
+// for kMaxRef / kFastRef.
+enum : int {
+  kMaxRef = 0, kFastRef = 1, kExactMax = 2, kLocal = 3, kTopKMax = 4,
+  kTopKFast = 5
+};
 
 template <int kMode>
 __global__ __launch_bounds__(kThreads, 1) void k_attn_fwd(AttnArgs a) {
   constexpr bool kExact = kMode == kExactMax;
-  constexpr bool kFast = kMode == kFastRef;
+  constexpr bool kTopK = kMode == kTopKMax || kMode == kTopKFast;
+  constexpr bool kFast = kMode == kFastRef || kMode == kTopKFast;
   constexpr bool kLoc = kMode == kLocal;
-  if (kMode == kMaxRef && a.wg_flag[blockIdx.x] == 0) return;  // done
+  if ((kMode == kMaxRef || kMode == kTopKMax) && a.wg_flag[blockIdx.x] == 0)
+    return;  // done
   // three K/V tile buffers of 2 x 16 KB
   __shared__ __attribute__((aligned(1024))) char tiles[3][2 * kTileBytes];
   __shared__ int wave_maxrow[kWaves];
   __shared__ int wave_ntiles[kWaves];
   // exact mode: each wave's maximum of the next tile, by step parity
   __shared__ unsigned tile_max[2][kWaves];
+  // Top-K mode: the four blocks' masks, the union of their selected
+  // positions (in L_t order) and, per step, which of the blocks take it
+  // (per step: position | blocks << 16)
+  __shared__ uint32_t tk_words[4][kMaskWords];
+  __shared__ int tk_step[kMaxTiles];
+  __shared__ int tk_count;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int lq = lane & 31, lh = lane >> 5;
   const int qsub = wave & 3, half = wave >> 2;
@@ -414,7 +432,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_fwd(AttnArgs a) {
   // order by stop point
   const int ewg = chunk * 4 + qsub;
   const bool valid = ewg < a.G * bps;
-  const int e = (!kLoc && a.border != nullptr && valid)
+  // Top-K: a workgroup's blocks are consecutive blocks of one head (neighbours
+  // in pi_Q, whose selections overlap most)
+  const int e = kTopK ? (valid ? (ewg % bps) * a.G + ewg / bps : ewg)
+                : (!kLoc && a.border != nullptr && valid)
                     ? a.border[((long long)bg * a.T + t) * (a.G * bps) + ewg]
                     : ewg;
 
@@ -443,9 +464,52 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_fwd(AttnArgs a) {
   // entries, query rows; indices, key rows) where the plain order of the
   // statements made seven.
   const int rg = gather_row(wave, lane);
+  if constexpr (kTopK) {
+    // the union of the four blocks' selected positions, in L_t order
+    const int hb = g * a.G + (valid ? e % a.G : 0);
+    const size_t blk = ((size_t)b * a.Hq + hb) * (a.N / kBlock) + t * bps +
+                       (valid ? e / a.G : 0);
+    if (half == 0)
+      tk_words[qsub][lane] = valid ? a.tmask[blk * kMaskWords + lane] : 0u;
+    __syncthreads();
+    if (wave == 0) {
+      const uint32_t w0 = tk_words[0][lane], w1 = tk_words[1][lane],
+                     w2 = tk_words[2][lane], w3 = tk_words[3][lane];
+      uint32_t u = w0 | w1 | w2 | w3;
+      const int cnt = __popc(u);
+      int incl = cnt;  // inclusive prefix sum over the lanes
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(incl, o);
+        if (lane >= o) incl += y;
+      }
+      int off = incl - cnt;
+      while (u != 0u) {
+        const int bit = __builtin_ctz(u);
+        u &= u - 1u;
+        const int blocks = (int)(((w0 >> bit) & 1u) | (((w1 >> bit) & 1u) << 1) |
+                                 (((w2 >> bit) & 1u) << 2) |
+                                 (((w3 >> bit) & 1u) << 3));
+        tk_step[off] = (32 * lane + bit) | (blocks << 16);
+        ++off;
+      }
+      if (lane == 63) tk_count = incl;
+    }
+    __syncthreads();
+  }
+  // Top-K: position of L_t that step s visits and the blocks that take it
+  // (wave-uniform; past the last step: the last step's, in bounds)
+  auto tk_entry = [&](int s) -> int {
+    return __builtin_amdgcn_readfirstlane(
+        tk_step[min(s, max(tk_count - 1, 0))]);
+  };
+  auto tk_position = [&](int s) -> int {
+    return min(tk_entry(s) & 0xffff, max(ntl - 1, 0));
+  };
   auto first_key = [&](int s) -> int {
     const bool computed = kLoc || s < ndiag_sparse || ntl == 0;
-    const int k = min(max(s - ndiag_sparse, 0), max(ntl - 1, 0));
+    const int k = kTopK ? tk_position(s)
+                        : min(max(s - ndiag_sparse, 0), max(ntl - 1, 0));
     const int32_t* src = ntl == 0 ? a.pi_q + rg : Lt + (size_t)k * kBlock + rg;
     const int x = kLoc ? 0 : *src;
     return computed ? seg0 + s * kBlock + rg : x;
@@ -461,8 +525,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_fwd(AttnArgs a) {
   int32_t* nI_ptr = a.n_I + bh * (a.N / kBlock) + I;
   // sparse passes: unconditional, no wait for it until used; the local pass
   // reads nothing the planner writes (it may run beside the planner)
-  const int nI_raw = kLoc ? 0 : *nI_ptr;
-  const int nI = (!valid || kLoc) ? 0 : kExact ? ntl : min(max(nI_raw, 0), ntl);
+  const int nI_raw = (kLoc || kTopK) ? 0 : *nI_ptr;
+  const int nI = (!valid || kLoc) ? 0
+                 : kExact ? ntl
+                 : kTopK  ? tk_count
+                          : min(max(nI_raw, 0), ntl);
   // my row: the local pass takes the segment's rows in their own order,
   // the sparse passes the rows of block I of pi_Q
   const int iq = kLoc ? seg0 + Ib * kBlock + 32 * half + lq
@@ -541,6 +608,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_fwd(AttnArgs a) {
   // lane fetches for tile s + 4 (steps past the last one load a harmless
   // in-bounds value); the local pass computes its indices.
   auto key_src = [&](int s, int row) -> const int32_t* {
+    if (kTopK)
+      return s < nsteps ? Lt + (size_t)tk_position(s) * kBlock + row
+                        : pq + (row & 63);
     return (s >= ndiag && s < nsteps) ? Lt + (size_t)(s - ndiag) * kBlock + row
                                       : pq + (row & 63);
   };
@@ -610,7 +680,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_fwd(AttnArgs a) {
     const bool local = s < ndiag;  // every step of the local pass
     // the local pass: block Ib sees key blocks 0 .. Ib, the last one masked
     if (kLoc && s == Ib) mask_local(s, cur);
-    bool act = valid && (kLoc ? s <= Ib : (s - ndiag) < nI);
+    bool act = valid && (kLoc    ? s <= Ib
+                         : kTopK ? ((tk_entry(s) >> (16 + qsub)) & 1) != 0
+                                 : (s - ndiag) < nI);
     if (kExact && !local) {
       // exact max test of tile s: both halves take max(own, other) of the
       // maxima posted with the tile's logits, before the last barrier
@@ -741,6 +813,15 @@ hipError_t launch_attention_sparse(const AttnArgs& a, hipStream_t s) {
   const int total = a.n_groups * a.wg_per_group;
   if (a.exact) {
     hipLaunchKernelGGL(k_attn_fwd<kExactMax>, dim3(total), dim3(kThreads), 0,
+                       s, a);
+    return hipGetLastError();
+  }
+  if (a.topk) {
+    hipLaunchKernelGGL(k_attn_fwd<kTopKFast>, dim3(total), dim3(kThreads), 0,
+                       s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_attn_fwd<kTopKMax>, dim3(total), dim3(kThreads), 0,
                        s, a);
     return hipGetLastError();
   }

@@ -80,6 +80,24 @@ struct StopArgs {
 };
 hipError_t launch_stop_scan(const StopArgs& a, hipStream_t s);
 
+// ---- per-block centroid Top-K selection (instead of the tau stop)
+constexpr int kMaskWords = kMaxTiles / 32;  // bitmask words per query block
+struct TopkArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const int32_t* pi_q;
+  const int32_t* L;
+  int64_t* scores;   // scratch: per (b, h) and block, one score per tile
+  uint32_t* tmask;   // out: [B, Hq, N / 64, kMaskWords] selected positions
+  int32_t* n_I;      // out: tiles selected per block
+  long long list_len;
+  int B, Hq, Hkv, N, S, T, G;
+  int K;             // tiles per block (>= 0)
+};
+hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
+// Bytes of the scores scratch: one int64 per (block, tile of its L_t).
+size_t topk_scratch_bytes(int B, int Hq, int S, int T);
+
 // Per (b, KV head, segment): its G (S / 64) query blocks by stop point
 // descending, for groups of at most kOrderMax blocks.
 constexpr int kOrderMax = 1024;
@@ -113,6 +131,8 @@ struct AttnArgs {
   const int32_t* border;  // per group: blocks by stop point (null: in order)
   int exact;       // 1: exact per-block max test instead of the stop points
   float exact_thr; // that test's threshold on the raw dot products (theta / kappa)
+  int topk;        // 1: per-block Top-K masks instead of the stop points
+  const uint32_t* tmask;  // [B, Hq, N / 64, kMaskWords]: Top-K selections
 };
 // The local pass (V converted to fp16, then every row's dense local window,
 // rows in their own order; needs nothing from the plan but its workspace)

@@ -25,7 +25,7 @@ struct Layout {
   size_t pool_part, pooled, vscore, blocksum, segsum, contrast, u;
   size_t key_a, idx_a, key_b, idx_b;
   size_t pi_k, L, pi_q, n_I, rcnt, rcum, qsum, kpart, kmax2, wg_flag, lse2,
-      border, olo, v16;
+      border, olo, v16, tmask;
   size_t total;
 };
 
@@ -111,6 +111,7 @@ Layout layout_of(const PlanDims& d) {
   L.border = take(nbh * (d.N / kBlock) * sizeof(int32_t));
   L.olo = take(nbh * d.N * kHeadDim * sizeof(uint16_t));
   L.v16 = take(nbg * d.N * kHeadDim * sizeof(uint16_t));
+  L.tmask = take(nbh * (d.N / kBlock) * kMaskWords * sizeof(uint32_t));
   L.total = off;
   return L;
 }
@@ -120,6 +121,7 @@ Layout layout_of(const PlanDims& d) {
 struct sa_plan {
   sa_params p;
   int32_t budget = -1;  // >= 0: fixed tile budget instead of the tau stop
+  int32_t topk = -1;    // >= 0: per-block Top-K selections (masks selected)
   double max_theta = std::numeric_limits<double>::quiet_NaN();  // exact test
   // n_I holds the stop points of the current settings (set by the stop
   // scan; cleared by every setter and by an exact-mode prefill, whose n_I
@@ -192,6 +194,10 @@ int build_from_kv_order(sa_plan* pl, hipStream_t s) {
 
 bool exact_mode(const sa_plan* pl) {
   return !std::isnan(pl->max_theta) && !(pl->p.flags & SA_LOCAL_ONLY);
+}
+
+bool topk_mode(const sa_plan* pl) {
+  return pl->topk >= 0 && !exact_mode(pl) && !(pl->p.flags & SA_LOCAL_ONLY);
 }
 
 // The sparse pass takes each group's blocks by stop point (small groups).
@@ -358,7 +364,9 @@ AttnArgs attn_args(const sa_plan* plan, const void* q, const void* k,
   a.olo = plan->at<uint16_t>(plan->lay.olo);
   a.local_only = (plan->p.flags & SA_LOCAL_ONLY) ? 1 : 0;
   a.local_steps = 0;
-  a.border = (!a.exact && block_order_used(d))
+  a.topk = topk_mode(plan) ? 1 : 0;
+  a.tmask = plan->at<uint32_t>(plan->lay.tmask);
+  a.border = (!a.exact && !a.topk && block_order_used(d))
                  ? plan->at<int32_t>(plan->lay.border)
                  : nullptr;
   return a;
@@ -366,7 +374,7 @@ AttnArgs attn_args(const sa_plan* plan, const void* q, const void* k,
 
 // The sparse passes, after rescanning stale stop points.
 int sparse_passes(const sa_plan* plan, const AttnArgs& a, hipStream_t stream) {
-  if (!a.exact && !plan->stops_valid) {
+  if (!a.exact && !a.topk && !plan->stops_valid) {
     const int rc = run_stop_scan(plan, stream);
     if (rc != SA_OK) return rc;
   }
@@ -455,6 +463,52 @@ int sparse_attn_plan_set_max_threshold(sa_plan* plan, double theta) {
   return SA_OK;
 }
 
+size_t sparse_attn_topk_scratch_bytes(const sa_plan* plan) {
+  if (plan == nullptr) return 0;
+  const PlanDims& d = plan->d;
+  return topk_scratch_bytes(d.B, d.Hq, d.S, d.T);
+}
+
+int sparse_attn_plan_set_topk(sa_plan* plan, int32_t tiles, void* scratch,
+                              size_t scratch_bytes, hipStream_t stream) {
+  if (plan == nullptr) return SA_ERR_NULL_POINTER;
+  if (tiles < 0) {  // back to the tau stop (or a budget)
+    plan->topk = -1;
+    plan->stops_valid = false;
+    return SA_OK;
+  }
+  const PlanDims& d = plan->d;
+  const size_t need = topk_scratch_bytes(d.B, d.Hq, d.S, d.T);
+  if (need > 0 && scratch == nullptr) return SA_ERR_NULL_POINTER;
+  if (scratch_bytes < need) return SA_ERR_WORKSPACE_TOO_SMALL;
+  if (reinterpret_cast<uintptr_t>(scratch) % 8 != 0) return SA_ERR_INVALID_ARG;
+  TopkArgs a;
+  a.q = static_cast<const uint16_t*>(plan->q);
+  a.k = static_cast<const uint16_t*>(plan->k);
+  a.pi_q = plan->at<int32_t>(plan->lay.pi_q);
+  a.L = plan->at<int32_t>(plan->lay.L);
+  a.scores = static_cast<int64_t*>(scratch);
+  a.tmask = plan->at<uint32_t>(plan->lay.tmask);
+  a.n_I = plan->at<int32_t>(plan->lay.n_I);
+  a.list_len = (long long)d.list_len;
+  a.B = d.B;
+  a.Hq = d.Hq;
+  a.Hkv = d.Hkv;
+  a.N = d.N;
+  a.S = d.S;
+  a.T = d.T;
+  a.G = d.G;
+  a.K = tiles;
+  // n_I now counts the selected tiles; leaving the mode rescans the stop
+  // points
+  plan->stops_valid = false;
+  plan->topk = -1;
+  const hipError_t e = launch_topk(a, stream);
+  if (e != hipSuccess) return SA_ERR_HIP;
+  plan->topk = tiles;
+  return SA_OK;
+}
+
 int sparse_attn_plan_set_budget(sa_plan* plan, int32_t tiles) {
   if (plan == nullptr) return SA_ERR_NULL_POINTER;
   plan->budget = tiles < 0 ? -1 : tiles;
@@ -483,6 +537,8 @@ size_t sparse_attn_plan_export_bytes(const sa_plan* plan, int what) {
     case SA_EXPORT_QUERY_SCORE: return nbh * d.N * sizeof(int64_t);
     case SA_EXPORT_CONTRAST: return nbg * d.T * kHeadDim * sizeof(int64_t);
     case SA_EXPORT_POOLED: return nbg * kHeadDim * sizeof(int64_t);
+    case SA_EXPORT_TOPK_MASK:
+      return nbh * (d.N / kBlock) * kMaskWords * sizeof(uint32_t);
     default: return 0;
   }
 }
@@ -504,6 +560,7 @@ int sparse_attn_plan_export(const sa_plan* plan, int what, void* host_dst,
     case SA_EXPORT_QUERY_SCORE: off = plan->lay.u; break;
     case SA_EXPORT_CONTRAST: off = plan->lay.contrast; break;
     case SA_EXPORT_POOLED: off = plan->lay.pooled; break;
+    case SA_EXPORT_TOPK_MASK: off = plan->lay.tmask; break;
   }
   hipError_t e = hipMemcpyAsync(host_dst, plan->ws + off, need,
                                 hipMemcpyDeviceToHost, stream);
@@ -522,6 +579,7 @@ int sparse_attn_plan_set_kv_order(sa_plan* plan, const void* pi_k,
                                 hipMemcpyDeviceToDevice, stream);
   if (e != hipSuccess) return SA_ERR_HIP;
   plan->stops_valid = false;
+  plan->topk = -1;  // the selections were made on the old lists
   const int rc = build_from_kv_order(plan, stream);
   return rc != SA_OK ? rc : run_stop_scan(plan, stream);
 }

@@ -38,7 +38,7 @@ def bf16_tensor_to_f64(t):
 
 
 def run_gpu(q, k, v, segment, tau, flags=0, kv_order=None, budget=None,
-            max_theta=None):
+            max_theta=None, topk=None):
     import torch
     import permuted_block_sparse_amd as pbs
     tq, tk, tv = to_device(q), to_device(k), to_device(v)
@@ -50,9 +50,12 @@ def run_gpu(q, k, v, segment, tau, flags=0, kv_order=None, budget=None,
     if kv_order is not None:
         pl.set_kv_order(torch.from_numpy(
             np.ascontiguousarray(kv_order, dtype=np.int32)).to("cuda:0"))
+    if topk is not None:
+        pl.set_topk(topk)
     o, lse = pbs.prefill(pl, tq, tk, tv, return_lse=True)
     torch.cuda.synchronize()
-    return {
+    extra = {"topk_masks": pl.topk_masks()} if topk is not None else {}
+    return {**extra,
         "o": bf16_tensor_to_f64(o), "lse": lse.cpu().numpy().astype(np.float64),
         "pi_k": pl.pi_k(), "pi_q": pl.pi_q(), "L": pl.restricted_lists(),
         "n_I": pl.n_I(), "key_score": pl.key_score(),
@@ -108,3 +111,12 @@ def assert_outputs_close(o_gpu, o_ref, lse_gpu=None, lse_ref=None, mask=None):
         le = np.abs(lse_gpu[mask] - lse_ref[mask]).max()
         assert le <= LSE_TOL, f"lse err {le}"
     return float(err.max()), mse
+
+
+def unpack_tile_mask(words, ntl):
+    """Bitmask words (uint32, bit p of word w = position 32 w + p) -> bool
+    per position; also asserts that no bit past ntl is set."""
+    bits = np.unpackbits(np.ascontiguousarray(words).view(np.uint8),
+                         bitorder="little").astype(bool)
+    assert not bits[ntl:].any(), "bits set past the end of L_t"
+    return bits[:ntl]

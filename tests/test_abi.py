@@ -25,7 +25,7 @@ def declared_functions():
 def test_every_declared_symbol_is_exported():
     lib = _lib.load()
     names = declared_functions()
-    assert len(names) == 12
+    assert len(names) == 14
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(_lib.EXPORTED_SYMBOLS)
@@ -108,6 +108,9 @@ def test_other_entry_points_reject_null():
     assert lib.sparse_attn_plan_export(None, 0, f, 8, None) == \
         _lib.SA_ERR_NULL_POINTER
     assert lib.sparse_attn_plan_export_bytes(None, 0) == 0
+    assert lib.sparse_attn_plan_set_topk(None, 3, f, 8, None) == \
+        _lib.SA_ERR_NULL_POINTER
+    assert lib.sparse_attn_topk_scratch_bytes(None) == 0
     lib.sparse_attn_plan_destroy(None)
 
 

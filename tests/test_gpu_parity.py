@@ -621,3 +621,101 @@ def test_non_current_streams():
     assert torch.equal(of.view(torch.int16), o_ref.view(torch.int16))
     assert torch.equal(lf, l_ref)
     del junk
+
+
+def _check_topk(q, k, v, S, K, flags=0):
+    from tests.gpu_helpers import unpack_tile_mask
+    pl = O.plan(q, k, S, flags=flags)
+    n_ref, m_ref, _ = O.topk_selection(q, k, pl, K)
+    g = run_gpu(q, k, v, S, 0.05, flags, topk=K)
+    assert_plan_equal(g, pl)
+    B, Hq, N = q.shape[:3]
+    for b in range(B):
+        for h in range(Hq):
+            for I in range(N // 64):
+                ntl = (I * 64 // S) * S // 64
+                got = unpack_tile_mask(g["topk_masks"][b, h, I], ntl)
+                assert np.array_equal(got, m_ref[(b, h, I)]), (K, b, h, I)
+    assert np.array_equal(g["n_I"], n_ref), K
+    o_ref, l_ref = O.attend(q, k, v, pl, n_ref, tile_mask=m_ref)
+    err, mse = assert_outputs_close(g["o"], o_ref, g["lse"], l_ref)
+    return err, mse, g, pl
+
+
+TOPK_CASES = [
+    # name, spec, S, Ks
+    ("gqa_n1024_s256", _spec(1, 4, 2, 1024, 49), 256, (0, 1, 5, 12)),
+    ("b2_n2048_s128", _spec(2, 2, 1, 2048, 51), 128, (3, 17)),
+    # 9 tiles per segment: selections and tile chunks end mid-word
+    ("ragged_s576_n2304", _spec(1, 4, 1, 2304, 52), 576, (2, 7, 30)),
+    # 256 blocks per (KV head, segment): two scoring workgroups; up to 192
+    # tiles per list: six tile chunks
+    ("two_chunks_s4096_n16384", _spec(1, 4, 1, 16384, 53, n_vert=64,
+                                      window=128), 4096, (40, 100)),
+]
+
+
+@pytest.mark.parametrize("name,spec,S,Ks", TOPK_CASES,
+                         ids=[c[0] for c in TOPK_CASES])
+def test_topk_parity(name, spec, S, Ks):
+    """Per-block centroid Top-K: the GPU's selections (bitmasks over the
+    positions of L_t) equal the oracle's bit for bit, n_I = min(K, t S /
+    64), and outputs match the oracle on those selections."""
+    q, k, v = make_stripe_inputs(spec)
+    for K in Ks:
+        say(f"[topk] {name} K={K}")
+        err, mse, g, pl = _check_topk(q, k, v, S, K)
+        say(f"   max_abs={err:.3g} mse={mse:.3g} mean_n_I="
+            f"{g['n_I'].mean():.2f}")
+
+
+def test_topk_worked_example_and_mode_changes():
+    """The hand-derived selection on the GPU plan (head dimension padded to
+    128): block 2 takes the e1 tile, block 3 the e2 tile, segment 2's
+    zero-query blocks the first positions. K >= all gives dense attention;
+    back to the tau stop with K < 0 the stop points are the oracle's again;
+    injecting a KV order ends the mode."""
+    import torch
+    from tests.gpu_helpers import unpack_tile_mask, to_device
+    import permuted_block_sparse_amd as pbs
+    N, S = 384, 128
+    qf = np.zeros((1, 1, N, 128), np.float32)
+    qf[0, 0, :128, 0] = 1.0
+    qf[0, 0, 128:192, 1] = 1.0
+    qf[0, 0, 192:256, 0] = 1.0
+    kf = np.zeros((1, 1, N, 128), np.float32)
+    kf[0, 0, :64, 0] = 1.0
+    kf[0, 0, 64:128, 1] = 1.0
+    q, k = _bits(qf), _bits(kf)
+    v = _bits(np.random.default_rng(54).standard_normal((1, 1, N, 128)))
+    say("[topk] worked example")
+    g = run_gpu(q, k, v, S, 0.05, topk=1)
+    got = {I: unpack_tile_mask(g["topk_masks"][0, 0, I],
+                               (I * 64 // S) * S // 64).astype(int).tolist()
+           for I in range(2, 6)}
+    assert got == {2: [1, 0], 3: [0, 1], 4: [1, 0, 0, 0], 5: [1, 0, 0, 0]}
+    spec = _spec(1, 4, 2, 1024, 55)
+    q, k, v = make_stripe_inputs(spec)
+    say("[topk] K >= all is dense")
+    od, ld = O.dense_causal(q, k, v)
+    g = run_gpu(q, k, v, 256, 0.05, topk=1000)
+    assert_outputs_close(g["o"], od, g["lse"], ld)
+    say("[topk] back to the tau stop, then a KV order injection")
+    tq, tk, tv = to_device(q), to_device(k), to_device(v)
+    p = pbs.plan(tq, tk, 256, 0.05)
+    p.set_topk(2)
+    pbs.prefill(p, tq, tk, tv)
+    assert (p.n_I()[:, :, 4:] == 2).all()
+    p.set_topk(-1)
+    o1 = pbs.prefill(p, tq, tk, tv)
+    pl = O.plan(q, k, 256)
+    n_tau, traces = O.stop_points(q, k, pl, 0.05)
+    assert not stop_mismatches(p.n_I(), n_tau, traces, 0.05)
+    p.set_topk(2)
+    p.set_kv_order(torch.arange(1024, dtype=torch.int32,
+                                device="cuda:0").repeat(1, 2, 1))
+    pbs.prefill(p, tq, tk, tv)
+    torch.cuda.synchronize()
+    pli = O.plan(q, k, 256, kv_order=np.tile(np.arange(1024), (1, 2, 1)))
+    n_i, tr_i = O.stop_points(q, k, pli, 0.05)
+    assert not stop_mismatches(p.n_I(), n_i, tr_i, 0.05)

@@ -11,10 +11,15 @@ GPU). The plan alone, the prefill alone and the two calls in order on one
 stream are timed as well.
 
 Besides the timed steps the run reports: the stop statistics (pair sparsity,
-visited tiles), MSE against dense attention (the same kernel at tau = 0,
-itself checked against the float64 oracle on sampled rows), the tau sweep of
-the workload, planner overhead, the attention kernel's MFMA roofline, and
-the CPU oracle timed on the host's cores on a bounded sample.
+tile density, visited tiles), MSE and attention recall against dense
+attention (the same kernel at tau = 0, itself checked against the float64
+oracle), the tau sweep of the workload, the variants at matched sparsity
+(uniform tile budget, per-block centroid Top-K, exact per-block maximum
+test), the segment-local KV order, planner overhead, the attention kernel's
+MFMA roofline, the other workloads (the tiny case, the 32K layer, the 128K
+Qwen-shaped layer over its segment lengths, the batch-4 64K ablation), and
+the CPU oracle timed on the host's cores on a bounded sample, which also
+checks the GPU run on that sample.
 """
 from __future__ import annotations
 
@@ -34,8 +39,9 @@ BF16_PEAK_TFLOPS = 2500.0     # MI355X dense bf16 MFMA (no sparsity)
 HBM_PEAK_GBS = 8000.0
 TILE_FLOP = 4 * 64 * 64 * 128  # QK^T + PV of one 64 x 64 tile, d = 128
 METRIC = "ms/layer sparse prefill attn @128K; sparsity & MSE; MFMA util vs bf16 peak"
-# query blocks in the CPU oracle's timed sample
+# query blocks and dense rows in the CPU oracle's timed sample
 CPU_SAMPLE_BLOCKS = 240
+CPU_SAMPLE_ROWS = 512
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_attn_fwd_traffic_n128k.json")
 ATTN_SOURCE = os.path.join(ROOT, "permuted_block_sparse_amd", "csrc",
                            "attn_kernel.hip")
@@ -57,6 +63,8 @@ def parse():
     ap.add_argument("--no-extras", action="store_true",
                     help="only the timed steps (for profiling runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-other-workloads", action="store_true",
+                    help="skip the reports of the other workloads")
     ap.add_argument("--profile-once", action="store_true",
                     help="one plan + one prefill, no timing (counter runs)")
     ap.add_argument("--plan-only", type=int, default=0, metavar="K",
@@ -275,13 +283,37 @@ def main():
         "flop_per_launch": flop_launch,
         "avg_launch_ms": round(attn_mean, 4)}
 
-    if not args.no_extras:
-        result.update(extras(args, cfg, q, k, v, tq, tk, tv, pl, out, S,
-                             tau, timed))
+    gpu = None
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(cfg, q, k, v, S, tau,
-                                              nb_total=B * Hq * nb)
+        # the GPU results the oracle's sample is checked against (the step's
+        # plan and output at the workload's tau; the dense run at tau = 0)
+        G = Hq // Hkv
+        import torch
+        o_dense = torch.empty_like(tq)
+        pl0 = pbs.plan(tq, tk, S, 0.0)
+        pbs.prefill(pl0, tq, tk, tv, out=o_dense)
+        pbs.prefill(pl, tq, tk, tv, out=out)
+        gpu = {"n_I": n_I, "pi_k": pl.pi_k()[:1, :1],
+               "pi_q": pl.pi_q()[:1, :G],
+               "L": pl.restricted_lists()[:1, :1],
+               "o": bf16_to_f64(out[:1, :G]),
+               "o_dense": bf16_to_f64(o_dense[:1, :1])}
+        del o_dense, pl0
+    if not args.no_extras:
+        result.update(extras(args, cfg, tq, tk, tv, S, tau))
+        if not args.no_other_workloads:
+            del out
+            result["workloads"] = workload_reports()
+    if gpu is not None:
+        result["cpu_baseline"] = cpu_baseline(cfg, q, k, v, S, tau, gpu)
     print(json.dumps(result), flush=True)
+
+
+def bf16_to_f64(t):
+    import torch
+    u = t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+    return (u.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(
+        np.float64)
 
 
 def selection_stats(n_I, N, S, pi_q=None):
@@ -394,265 +426,384 @@ def plan_kernel_bytes(B, Hq, Hkv, N, S, d, scan_tiles, scanning=True):
     return res
 
 
-def extras(args, cfg, q, k, v, tq, tk, tv, pl, out, S, tau, timed):
-    """tau sweep, dense reference, MSE, sampled-row validation."""
+def kernel_tiles(n_I, B, Hq, N, S):
+    """64 x 64 tiles the attention kernel computes in one prefill: the local
+    pass takes every segment's rows in their own order, block i of a
+    segment against its key blocks 0 .. i (bps (bps + 1) / 2 tiles per
+    segment and head), and the sparse pass n_I tiles per block."""
+    bps, T = S // 64, N // S
+    return B * Hq * T * bps * (bps + 1) // 2 + int(np.asarray(n_I).sum())
+
+
+def hip_ms(fn, reps):
+    """Median of `reps` calls of fn, timed by HIP events on torch's current
+    stream (the stream every launch of fn goes to)."""
+    import torch
+    stream = torch.cuda.current_stream()
+    ts = []
+    for _ in range(reps):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        ts.append(a.elapsed_time(b))
+    return float(np.median(ts))
+
+
+def recall_stats(lse_sel, lse_dense):
+    """Share of each row's dense causal attention mass on its selected set:
+    exp(lse over Sel(i) - lse over every causal key)."""
+    import torch
+    r = torch.exp(lse_sel - lse_dense)
+    per_head = r.mean(dim=(0, 2))
+    return {"recall_mean": float("%.4g" % r.mean().item()),
+            "recall_min": float("%.4g" % r.min().item()),
+            "recall_head_mean_min": float("%.4g" % per_head.min().item())}
+
+
+def error_stats(o, ref, per_head=False):
+    """MSE (and max-abs) of o against ref over every element; per query head
+    when asked."""
+    diff = o.float() - ref.float()
+    sq = diff * diff
+    out = {"mse_vs_dense": float(sq.mean().item()),
+           "max_abs_vs_dense": float(diff.abs().max().item())}
+    ph = sq.mean(dim=(0, 2, 3)).cpu().numpy()
+    out["mse_per_head_max"] = float(ph.max())
+    if per_head:
+        out["mse_per_head"] = [float("%.3g" % x) for x in ph]
+    return out
+
+
+def measure(tq, tk, tv, S, tau, flags=0, setup=None, dense=None,
+            reps=3, fused=False, per_head=False):
+    """One selection on resident inputs: prefill time (HIP events, median of
+    `reps`), selection statistics, the attention kernel's visited-tile rate
+    and roofline fraction, and against `dense` ((o, lse) of the tau = 0 run)
+    the MSE and the attention recall. setup(plan) applies a setter (budget,
+    Top-K, threshold) before the prefills; fused also times the plan alone
+    and the whole step (sparse_attn_forward, local windows on a second
+    stream)."""
     import torch
     import permuted_block_sparse_amd as pbs
-    import oracle as O  # only for the sampled-row validation
+    B, Hq, N, d = tq.shape
+    res = {"segment": S, "tau": tau, "flags": flags}
+    if fused:
+        side = torch.cuda.Stream()
+        res["plan_ms"] = round(hip_ms(
+            lambda: pbs.plan(tq, tk, S, tau, flags=flags), reps), 4)
+        o_f = torch.empty_like(tq)
+        pbs.forward(tq, tk, tv, S, tau, flags=flags, out=o_f,
+                    side_stream=side)
+        res["step_ms"] = round(hip_ms(
+            lambda: pbs.forward(tq, tk, tv, S, tau, flags=flags, out=o_f,
+                                side_stream=side), reps), 4)
+        del o_f
+    pl = pbs.plan(tq, tk, S, tau, flags=flags)
+    if setup is not None:
+        res["setup_ms"] = round(hip_ms(lambda: setup(pl), 1), 4)
+    o = torch.empty_like(tq)
+    pbs.prefill(pl, tq, tk, tv, out=o)   # rescans after a setter
+    ms = hip_ms(lambda: pbs.prefill(pl, tq, tk, tv, out=o), reps)
+    _, lse = pbs.prefill(pl, tq, tk, tv, out=o, return_lse=True)
+    n_I = pl.n_I()
+    st = selection_stats(n_I, N, S, pl.pi_q())
+    tiles = kernel_tiles(n_I, B, Hq, N, S)
+    tflops = tiles * TILE_FLOP / (ms * 1e-3) / 1e12
+    res.update({"prefill_ms": round(ms, 4),
+                "pair_sparsity": round(st["pair_sparsity"], 5),
+                "tile_density": round(st["tile_density"], 5),
+                "mean_n_I": round(float(n_I.mean()), 2),
+                "visited_sparse_tiles": st["visited_sparse_tiles"],
+                "kernel_tiles": tiles,
+                "visited_tile_tflops": round(tflops, 1),
+                "frac": round(tflops / BF16_PEAK_TFLOPS, 4)})
+    if dense is not None:
+        res.update(error_stats(o, dense[0], per_head))
+        res.update(recall_stats(lse, dense[1]))
+    return res, pl, o, lse
 
-    def bf16_tensor_to_f64(t):
-        u = t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
-        return (u.astype(np.uint32) << np.uint32(16)).view(
-            np.float32).astype(np.float64)
 
-    spec = cfg.spec
-    B, Hq, Hkv, N = spec.batch, spec.heads_q, spec.heads_kv, spec.seq_len
-    T = N // S
-    pi_q = pl.pi_q()
+def dense_reference(tq, tk, tv, S, flags=0):
+    """The same kernel at tau = 0 visits every tile: dense causal attention
+    (checked against the float64 oracle by the GPU tests). Returns
+    (o, lse, prefill ms)."""
+    import torch
+    import permuted_block_sparse_amd as pbs
+    pl = pbs.plan(tq, tk, S, 0.0, flags=flags)
+    o = torch.empty_like(tq)
+    pbs.prefill(pl, tq, tk, tv, out=o)
+    ms = hip_ms(lambda: pbs.prefill(pl, tq, tk, tv, out=o), 2)
+    _, lse = pbs.prefill(pl, tq, tk, tv, out=o, return_lse=True)
+    return o, lse, ms
+
+
+def matched_budget(n_tau_total, B, Hq, N, S):
+    """Smallest uniform tile count K whose visited tiles (min(K, t S / 64)
+    per block of segment t) reach n_tau_total."""
+    T, bps = N // S, S // 64
+    caps = np.repeat(np.arange(T) * bps, B * Hq * bps)
+    lo, hi = 0, int(caps.max())
+    while lo < hi:
+        mid = (lo + hi) // 2
+        if int(np.minimum(caps, mid).sum()) >= n_tau_total:
+            hi = mid
+        else:
+            lo = mid + 1
+    return lo
+
+
+def extras(args, cfg, tq, tk, tv, S, tau):
+    """The headline workload's sweeps and variants: tau sweep against dense
+    attention, dense local window only, and at matched sparsity the fixed
+    budget, the per-block centroid Top-K and the exact per-block maximum
+    test; the segment-local KV order."""
+    import permuted_block_sparse_amd as pbs
+    B, Hq, N, d = tq.shape
     res = {}
-    # dense reference: the same kernel with tau = 0 visits every tile
-    pl.set_tau(0.0)
-    dense = torch.empty_like(tq)
-    dense_ms, _ = timed(lambda: pbs.prefill(pl, tq, tk, tv, out=dense), 2)
-    _, lse_dense = pbs.prefill(pl, tq, tk, tv, out=dense, return_lse=True)
+    o_d, l_d, dense_ms = dense_reference(tq, tk, tv, S)
+    dense = (o_d, l_d)
     log(f"[bench] tau=0 (dense) prefill {dense_ms:.3f} ms")
-
-    def recall_stats(lse_sel):
-        # share of each row's dense causal attention mass on its selected
-        # set: exp(lse over Sel(i) - lse over every causal key)
-        r = torch.exp(lse_sel - lse_dense)
-        per_head = r.mean(dim=(0, 2))
-        return {"recall_mean": float("%.4g" % r.mean().item()),
-                "recall_min": float("%.4g" % r.min().item()),
-                "recall_head_mean_min": float("%.4g" % per_head.min().item())}
     sweep = []
-    taus = sorted(set(cfg.taus) | {tau})
-    for t_ in taus:
-        pl.set_tau(t_)
-        o_t = torch.empty_like(tq)
-        ms, _ = timed(lambda: pbs.prefill(pl, tq, tk, tv, out=o_t), 3)
-        st = selection_stats(pl.n_I(), N, S, pi_q)
-        sp = st["pair_sparsity"]
-        diff = (o_t.float() - dense.float())
-        mse = float((diff * diff).mean().item())
-        per_head = (diff * diff).mean(dim=(0, 2, 3)).cpu().numpy()
-        _, lse_t = pbs.prefill(pl, tq, tk, tv, out=o_t, return_lse=True)
-        sweep.append({"tau": t_, "prefill_ms": round(ms, 4),
-                      "pair_sparsity": round(float(sp), 5),
-                      "tile_density": round(st["tile_density"], 5),
-                      "mse_vs_dense": mse,
-                      "mse_per_head_max": float(per_head.max()),
-                      "speedup_vs_dense": round(dense_ms / ms, 3),
-                      **recall_stats(lse_t)})
-        log(f"[bench] tau={t_}: {ms:.3f} ms sparsity={sp:.4f} mse={mse:.3g}")
-    pl.set_tau(tau)
+    for t_ in sorted(set(cfg.taus) | {tau}):
+        r, *_ = measure(tq, tk, tv, S, t_, dense=dense)
+        r["speedup_vs_dense"] = round(dense_ms / r["prefill_ms"], 3)
+        sweep.append(r)
+        log(f"[bench] tau={t_}: {r['prefill_ms']:.3f} ms sparsity="
+            f"{r['pair_sparsity']:.4f} mse={r['mse_vs_dense']:.3g}")
     res["tau_sweep"] = sweep
     res["dense_prefill_ms"] = round(dense_ms, 4)
     res["no_early_stop"] = {"note": "SA_NO_EARLYSTOP visits every tile: "
-                                    "the tau = 0 run above",
+                                    "the tau = 0 run",
                             "prefill_ms": round(dense_ms, 4)}
+    r, *_ = measure(tq, tk, tv, S, tau, flags=pbs.SA_LOCAL_ONLY, dense=dense)
+    res["local_window_only"] = r
+    log(f"[bench] local window only: {r}")
 
-    # baseline of the component ablation: the dense local window only
-    pl_loc = pbs.plan(tq, tk, S, tau, flags=pbs.SA_LOCAL_ONLY)
-    o_loc = torch.empty_like(tq)
-    loc_ms, _ = timed(lambda: pbs.prefill(pl_loc, tq, tk, tv, out=o_loc), 3)
-    _, lse_loc = pbs.prefill(pl_loc, tq, tk, tv, out=o_loc, return_lse=True)
-    diff = (o_loc.float() - dense.float())
-    st = selection_stats(pl_loc.n_I(), N, S, pi_q)
-    res["local_window_only"] = {
-        "prefill_ms": round(loc_ms, 4),
-        "pair_sparsity": round(st["pair_sparsity"], 5),
-        "tile_density": round(st["tile_density"], 5),
-        "mse_vs_dense": float((diff * diff).mean().item()),
-        **recall_stats(lse_loc)}
-    log(f"[bench] local window only: {res['local_window_only']}")
-    del pl_loc, o_loc, lse_loc
+    # matched sparsity: the uniform budget and the per-block Top-K get the
+    # smallest K whose visited tiles reach the tau stop's
+    base = [x for x in sweep if x["tau"] == tau][0]
+    n_tau = base["visited_sparse_tiles"]
+    K = matched_budget(n_tau, B, Hq, N, S)
+    r, *_ = measure(tq, tk, tv, S, tau, setup=lambda p: p.set_budget(K),
+                    dense=dense)
+    r.update({"budget_tiles": K, "tau_visited_tiles": n_tau})
+    res["fixed_budget_matched"] = r
+    log(f"[bench] fixed budget (matched): {r}")
+    r, *_ = measure(tq, tk, tv, S, tau, setup=lambda p: p.set_topk(K),
+                    dense=dense)
+    r.update({"topk_tiles": K, "tau_visited_tiles": n_tau,
+              "note": "setup_ms: exact scoring of every tile of every L_t "
+                      "(fp64 MFMA) and the per-block selection"})
+    res["topk_centroid_matched"] = r
+    log(f"[bench] per-block centroid Top-K (matched): {r}")
 
-    # fixed tile budget at matched sparsity: the smallest K whose visited
-    # tiles (min(K, t S / 64) per block) reach the tau stop's total
-    pl.set_tau(tau)
-    pbs.prefill(pl, tq, tk, tv, out=out)
-    visited_tau = int(pl.n_I().sum())
-    bps = S // 64
-    caps = np.repeat(np.arange(T) * bps, B * Hq * bps)
-    lo_k, hi_k = 0, int(caps.max())
-    while lo_k < hi_k:
-        mid = (lo_k + hi_k) // 2
-        if int(np.minimum(caps, mid).sum()) >= visited_tau:
-            hi_k = mid
-        else:
-            lo_k = mid + 1
-    K = lo_k
-    pl.set_budget(K)
-    o_b = torch.empty_like(tq)
-    b_ms, _ = timed(lambda: pbs.prefill(pl, tq, tk, tv, out=o_b), 3)
-    _, lse_b = pbs.prefill(pl, tq, tk, tv, out=o_b, return_lse=True)
-    n_b = pl.n_I()
-    pl.set_budget(-1)
-    st = selection_stats(n_b, N, S, pi_q)
-    diff = (o_b.float() - dense.float())
-    res["fixed_budget_matched"] = {
-        "budget_tiles": K, "visited_tiles": int(n_b.sum()),
-        "tau_visited_tiles": visited_tau,
-        "prefill_ms": round(b_ms, 4),
-        "pair_sparsity": round(st["pair_sparsity"], 5),
-        "tile_density": round(st["tile_density"], 5),
-        "mse_vs_dense": float((diff * diff).mean().item()),
-        **recall_stats(lse_b)}
-    log(f"[bench] fixed budget (matched): {res['fixed_budget_matched']}")
-    del o_b, lse_b
+    # exact per-block max test: theta bisected until the attended tiles
+    # match the tau stop's
+    pl = pbs.plan(tq, tk, S, tau)
+    o = torch_empty_like(tq)
 
-    # exact per-block max test (the BSFA variant): every tile scored
-    # exactly; the threshold is bisected until the attended tiles match the
-    # tau stop's visited tiles
     def exact_count(theta):
         pl.set_max_threshold(theta)
-        pbs.prefill(pl, tq, tk, tv, out=out)
+        pbs.prefill(pl, tq, tk, tv, out=o)
         return int(pl.n_I().sum())
     lo_t, hi_t = 0.0, 4.0
-    while exact_count(hi_t) > visited_tau:
+    while exact_count(hi_t) > n_tau:
         hi_t *= 2.0
-    while exact_count(lo_t) < visited_tau:
+    while exact_count(lo_t) < n_tau:
         lo_t -= 4.0
     for _ in range(16):
         mid = 0.5 * (lo_t + hi_t)
-        if exact_count(mid) >= visited_tau:
+        if exact_count(mid) >= n_tau:
             lo_t = mid
         else:
             hi_t = mid
-    pl.set_max_threshold(lo_t)
-    o_x = torch.empty_like(tq)
-    x_ms, _ = timed(lambda: pbs.prefill(pl, tq, tk, tv, out=o_x), 3)
-    _, lse_x = pbs.prefill(pl, tq, tk, tv, out=o_x, return_lse=True)
-    n_x = pl.n_I()
-    pl.set_max_threshold(float("nan"))
-    st = selection_stats(n_x, N, S, pi_q)
-    diff = (o_x.float() - dense.float())
-    res["exact_max_matched"] = {
-        "theta": round(lo_t, 5), "attended_tiles": int(n_x.sum()),
-        "scored_tiles": int(sum(B * Hq * bps * t * bps for t in range(T))),
-        "tau_visited_tiles": visited_tau,
-        "prefill_ms": round(x_ms, 4),
-        "pair_sparsity": round(st["pair_sparsity"], 5),
-        "tile_density": round(st["tile_density"], 5),
-        "mse_vs_dense": float((diff * diff).mean().item()),
-        **recall_stats(lse_x)}
-    log(f"[bench] exact max test (matched): {res['exact_max_matched']}")
-    del o_x, lse_x
+    del pl, o
+    r, *_ = measure(tq, tk, tv, S, tau,
+                    setup=lambda p: p.set_max_threshold(lo_t), dense=dense)
+    T, bps = N // S, S // 64
+    r.update({"theta": round(lo_t, 5), "tau_visited_tiles": n_tau,
+              "scored_tiles": int(sum(B * Hq * bps * t * bps
+                                      for t in range(T)))})
+    res["exact_max_matched"] = r
+    log(f"[bench] exact max test (matched): {r}")
 
-    # segment-local key order (the PBS-Attn variant) at the same tau
-    plan_seg_ms, _ = timed(
-        lambda: pbs.plan(tq, tk, S, tau, flags=pbs.SA_SEGMENT_KV), 3)
-    pl_seg = pbs.plan(tq, tk, S, tau, flags=pbs.SA_SEGMENT_KV)
-    o_seg = torch.empty_like(tq)
-    seg_ms, _ = timed(lambda: pbs.prefill(pl_seg, tq, tk, tv, out=o_seg), 3)
-    _, lse_seg = pbs.prefill(pl_seg, tq, tk, tv, out=o_seg, return_lse=True)
-    n_seg = pl_seg.n_I()
-    st = selection_stats(n_seg, N, S, pl_seg.pi_q())
-    diff = (o_seg.float() - dense.float())
-    res["segment_kv_order"] = {
-        "tau": tau, "plan_ms": round(plan_seg_ms, 4),
-        "prefill_ms": round(seg_ms, 4),
-        "pair_sparsity": round(st["pair_sparsity"], 5),
-        "tile_density": round(st["tile_density"], 5),
-        "mse_vs_dense": float((diff * diff).mean().item()),
-        **recall_stats(lse_seg)}
-    log(f"[bench] segment-local KV order: {res['segment_kv_order']}")
-    del pl_seg, o_seg, lse_seg
-
-    # sampled validation at full size in the timed launch configuration:
-    # KV group 0's plan against the oracle, and sampled blocks' stop points
-    # and outputs (and the dense reference on sampled rows)
-    log("[bench] validating sampled blocks against the oracle")
-    G = Hq // Hkv
-    qs = np.ascontiguousarray(q[:1, :G])
-    ks = np.ascontiguousarray(k[:1, :1])
-    vs = np.ascontiguousarray(v[:1, :1])
-    ref = O.plan(qs, ks, S)
-    ok_plan = (np.array_equal(pl.pi_k()[0, 0], ref.pi_k[0, 0])
-               and np.array_equal(pl.pi_q()[0, :G], ref.pi_q[0])
-               and np.array_equal(pl.restricted_lists()[0, 0], ref.L[0, 0]))
-    rng = np.random.default_rng(0)
-    nb = N // 64
-    blocks = [(0, int(h), int(I)) for h, I in
-              zip(rng.integers(0, G, 8), rng.integers(nb // 8, nb, 8))]
-    blocks.append((0, 0, nb - 1))
-    n_ref, traces = O.stop_points(qs, ks, ref, tau, blocks=blocks)
-    pl.set_tau(tau)
-    pbs.prefill(pl, tq, tk, tv, out=out)
-    n_gpu = pl.n_I()[:1, :G]
-    ties = 0
-    n_use = n_ref.copy()
-    for b, h, I in blocks:
-        if n_gpu[b, h, I] != n_ref[b, h, I]:
-            m = int(min(n_gpu[b, h, I], n_ref[b, h, I]))
-            assert abs(traces[(b, h, I)][m] - tau) <= 1e-4 * tau
-            ties += 1
-            n_use[b, h, I] = n_gpu[b, h, I]
-    o_ref, _ = O.attend(qs, ks, vs, ref, n_use, blocks=blocks)
-    o_gpu = bf16_tensor_to_f64(out[:1, :G])
-    mask = ~np.isnan(o_ref[..., 0])
-    err = float(np.abs(o_gpu[mask] - o_ref[mask]).max())
-    mse_s = float(np.mean((o_gpu[mask] - o_ref[mask]) ** 2))
-    rows = rng.integers(0, N, 16)
-    od, _ = O.dense_causal(qs, ks, vs, rows=rows, heads=[(0, 0)])
-    dg = bf16_tensor_to_f64(dense[:1, :1])
-    derr = float(np.abs(dg[0, 0, rows] - od[0, 0, rows]).max())
-    res["validation"] = {
-        "plan_group0_bit_exact": bool(ok_plan),
-        "sampled_blocks": len(blocks), "stop_ties": ties,
-        "stop_points_equal": bool(all(n_gpu[b, h, I] == n_use[b, h, I]
-                                      for b, h, I in blocks)),
-        "max_abs_err": err, "mse": mse_s,
-        "dense_sampled_rows_max_abs_err": derr,
-        "within_tolerance": bool(err <= 2e-2 and mse_s <= 1e-4
-                                 and derr <= 2e-2 and ok_plan)}
-    log(f"[bench] validation: {res['validation']}")
+    r, *_ = measure(tq, tk, tv, S, tau, flags=pbs.SA_SEGMENT_KV, dense=dense,
+                    fused=True)
+    res["segment_kv_order"] = r
+    log(f"[bench] segment-local KV order: {r}")
     return res
 
 
-def cpu_baseline(cfg, q, k, v, S, tau, nb_total):
-    """The oracle, as it stands, on a bounded sample of the workload: the
-    full plan of one KV group plus stop points and attention of
-    CPU_SAMPLE_BLOCKS seeded random query blocks of that group (about 10 s of
-    CPU work at 128K); extrapolated linearly to the whole layer (plan x
-    number of KV groups, attention x number of query blocks)."""
+def torch_empty_like(x):
+    import torch
+    return torch.empty_like(x)
+
+
+def upload(x):
+    import torch
+    return torch.from_numpy(x.view(np.int16)).to("cuda:0").view(torch.bfloat16)
+
+
+def workload_reports():
+    """The other workloads at their full sizes, each on its own inputs: the
+    tiny causal case, the 32K Llama-shaped layer, the 128K Qwen-shaped layer
+    over its segment lengths (per-head MSE), and the batch-4 64K ablation
+    (full S2O, KV permutation only, tau = 0 against plain dense attention
+    with the identity orders)."""
+    import torch
+    import permuted_block_sparse_amd as pbs
+    from synthetic import get_config, make_stripe_inputs
+    out = {}
+    for cid in (1, 2, 4, 5):
+        cfg = get_config(cid)
+        t0 = time.time()
+        q, k, v = make_stripe_inputs(cfg.spec)
+        log(f"[bench] workload {cfg.name}: inputs in {time.time() - t0:.1f}s")
+        tq, tk, tv = upload(q), upload(k), upload(v)
+        del q, k, v
+        o_d, l_d, dense_ms = dense_reference(tq, tk, tv, cfg.segment)
+        rep = {"workload": cfg.name, "shape": list(tq.shape),
+               "dense_prefill_ms": round(dense_ms, 4), "runs": []}
+        if cid == 4:
+            runs = [(S_, cfg.tau, 0) for S_ in cfg.segments]
+        elif cid == 5:
+            runs = [(cfg.segment, cfg.tau, 0),
+                    (cfg.segment, cfg.tau, pbs.SA_NO_QPERM)]
+        else:
+            runs = [(cfg.segment, cfg.tau, 0)]
+        for S_, t_, fl in runs:
+            r, *_ = measure(tq, tk, tv, S_, t_, flags=fl, dense=(o_d, l_d),
+                            fused=True, per_head=(cid == 4))
+            r["speedup_vs_dense"] = round(dense_ms / r["prefill_ms"], 3)
+            if cid == 5:
+                r["variant"] = "kv_perm_only" if fl else "s2o"
+            rep["runs"].append(r)
+            log(f"[bench] {cfg.name} S={S_} tau={t_} flags={fl}: "
+                f"{r['prefill_ms']:.3f} ms sparsity {r['pair_sparsity']:.4f}"
+                f" mse {r['mse_vs_dense']:.3g}")
+        if cid == 5:
+            # tau = 0 with the method's orders against plain dense causal
+            # flash attention (identity orders): the same attention up to
+            # the order in which each row's keys are added
+            o_i, l_i, ms_i = dense_reference(
+                tq, tk, tv, cfg.segment,
+                flags=pbs.SA_NO_QPERM | pbs.SA_NO_KVPERM)
+            diff = (o_d.float() - o_i.float())
+            rep["tau0_vs_identity_order_dense"] = {
+                "variant": "tau0", "prefill_ms": round(dense_ms, 4),
+                "identity_order_prefill_ms": round(ms_i, 4),
+                "max_abs": float(diff.abs().max().item()),
+                "mse": float((diff * diff).mean().item()),
+                "lse_max_abs": float((l_d - l_i).abs().max().item())}
+            log(f"[bench] tau=0 vs identity-order dense: "
+                f"{rep['tau0_vs_identity_order_dense']}")
+            del o_i, l_i
+        out[cfg.name] = rep
+        del tq, tk, tv, o_d, l_d
+        torch.cuda.empty_cache()
+    return out
+
+
+def cpu_baseline(cfg, q, k, v, S, tau, gpu):
+    """The oracle, as it stands, on a bounded sample of the workload, timed
+    in three parts on the host's cores (BLAS threads pinned to the cores the
+    process may use): the plan of one KV group (integer ranking), the stop
+    points and attention of CPU_SAMPLE_BLOCKS seeded random query blocks of
+    that group, and dense causal attention of CPU_SAMPLE_ROWS seeded rows of
+    one head; each extrapolated linearly to the layer (plan x KV groups,
+    attention x query blocks, dense x rows). The same sample checks the GPU
+    run (`gpu`: plan exports, stop points, outputs and the tau = 0 output):
+    plan bit-exact, stop points equal up to near-tau ties, outputs within
+    2e-2 max-abs and 1e-4 MSE."""
     import oracle as O
+    cores = len(os.sched_getaffinity(0))
     try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()]
-                      or [1])
+        from threadpoolctl import threadpool_info, threadpool_limits
+        limiter = threadpool_limits(limits=cores)
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()]
+                   or [1])
     except Exception:
-        threads = len(os.sched_getaffinity(0))
+        limiter, blas = None, None
     spec = cfg.spec
     G = spec.heads_q // spec.heads_kv
     qs = np.ascontiguousarray(q[:1, :G])
     ks = np.ascontiguousarray(k[:1, :1])
     vs = np.ascontiguousarray(v[:1, :1])
+    N = spec.seq_len
+    nb = N // 64
     log("[bench] cpu baseline: oracle plan of one KV group")
     t0 = time.perf_counter()
     ref = O.plan(qs, ks, S)
     t_plan = time.perf_counter() - t0
-    nb = spec.seq_len // 64
     rng = np.random.default_rng(1)
     blocks = [(0, int(h), int(I)) for h, I in
               zip(rng.integers(0, G, CPU_SAMPLE_BLOCKS),
                   rng.integers(0, nb, CPU_SAMPLE_BLOCKS))]
+    blocks.append((0, 0, nb - 1))
     log(f"[bench] cpu baseline: oracle stop points + attention of "
         f"{len(blocks)} blocks")
     t0 = time.perf_counter()
-    n_I, _ = O.stop_points(qs, ks, ref, tau, blocks=blocks)
-    O.attend(qs, ks, vs, ref, n_I, blocks=blocks)
-    t_blk = (time.perf_counter() - t0) / len(blocks)
+    n_ref, traces = O.stop_points(qs, ks, ref, tau, blocks=blocks)
+    t_stop = time.perf_counter() - t0
+    n_use = n_ref.copy()
+    ties = 0
+    n_gpu = gpu["n_I"][:1, :G]
+    for b, h, I in blocks:
+        if n_gpu[b, h, I] != n_ref[b, h, I]:
+            m = int(min(n_gpu[b, h, I], n_ref[b, h, I]))
+            if abs(traces[(b, h, I)][m] - tau) <= 1e-4 * tau:
+                ties += 1
+                n_use[b, h, I] = n_gpu[b, h, I]
+    t0 = time.perf_counter()
+    o_ref, _ = O.attend(qs, ks, vs, ref, n_use, blocks=blocks)
+    t_att = time.perf_counter() - t0
+    rows = rng.integers(0, N, CPU_SAMPLE_ROWS)
+    log(f"[bench] cpu baseline: oracle dense attention of {len(rows)} rows")
+    t0 = time.perf_counter()
+    od, _ = O.dense_causal(qs, ks, vs, rows=rows, heads=[(0, 0)])
+    t_dense = time.perf_counter() - t0
+    if limiter is not None:
+        limiter.unregister()
     groups = spec.batch * spec.heads_kv
-    est_s = t_plan * groups + t_blk * nb_total
-    return {"value": round(est_s * 1e3, 1), "unit": "ms/layer",
-            "cores": int(threads), "kind": "oracle",
+    nblk = spec.batch * spec.heads_q * nb
+    nrows = spec.batch * spec.heads_q * N
+    plan_ms = t_plan * groups * 1e3
+    s2o_ms = (t_stop + t_att) / len(blocks) * nblk * 1e3
+    dense_ms = t_dense / len(rows) * nrows * 1e3
+    mask = ~np.isnan(o_ref[..., 0])
+    err = float(np.abs(gpu["o"][mask] - o_ref[mask]).max())
+    mse = float(np.mean((gpu["o"][mask] - o_ref[mask]) ** 2))
+    derr = float(np.abs(gpu["o_dense"][0, 0, rows] - od[0, 0, rows]).max())
+    ok_plan = (np.array_equal(gpu["pi_k"][0, 0], ref.pi_k[0, 0])
+               and np.array_equal(gpu["pi_q"][0, :G], ref.pi_q[0])
+               and np.array_equal(gpu["L"][0, 0], ref.L[0, 0]))
+    stops_ok = all(n_gpu[b, h, I] == n_use[b, h, I] for b, h, I in blocks)
+    return {"value": round(plan_ms + s2o_ms, 1), "unit": "ms/layer",
+            "cores": cores, "blas_threads": blas, "kind": "oracle",
+            "parts_ms": {"plan": round(plan_ms, 1),
+                         "s2o_attention": round(s2o_ms, 1),
+                         "dense_attention": round(dense_ms, 1)},
             "sample": f"oracle plan of 1 of {groups} KV groups "
-                      f"({t_plan:.2f} s) + stop points and attention of "
-                      f"{len(blocks)} of {nb_total} query blocks ({t_blk * 1e3:.1f} ms "
-                      f"each), extrapolated linearly to the layer",
-            "extrapolated": True}
+                      f"({t_plan:.2f} s), stop points and attention of "
+                      f"{len(blocks)} of {nblk} query blocks "
+                      f"({(t_stop + t_att) * 1e3 / len(blocks):.1f} ms each), "
+                      f"dense attention of {len(rows)} of {nrows} rows "
+                      f"({t_dense * 1e3 / len(rows):.2f} ms each); each "
+                      f"extrapolated linearly to the layer; value = plan + "
+                      f"S2O attention",
+            "extrapolated": True,
+            "validation": {
+                "plan_group0_bit_exact": bool(ok_plan),
+                "sampled_blocks": len(blocks), "stop_ties": ties,
+                "stop_points_equal": bool(stops_ok),
+                "max_abs_err": err, "mse": mse,
+                "dense_sampled_rows_max_abs_err": derr,
+                "within_tolerance": bool(err <= 2e-2 and mse <= 1e-4
+                                         and derr <= 2e-2 and ok_plan
+                                         and stops_ok)}}
 
 
 if __name__ == "__main__":

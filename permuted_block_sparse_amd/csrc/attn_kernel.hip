@@ -12,8 +12,9 @@
 // (rows t S + 64 i ..) against key blocks 0 .. i of the segment, only the
 // last one masked. It writes the normalised result to O (bf16), its
 // residual below that bf16 value to a scratch array (bf16; the two carry
-// about 16 significant bits of the fp32 result) and the log2-sum-exp of
-// each row. The sparse pass takes the blocks of pi_Q: each row resumes from
+// about 16 significant bits of the fp32 result; only for half-rows with a
+// value of magnitude >= 1, where the rounding would matter) and the
+// log2-sum-exp of each row. The sparse pass takes the blocks of pi_Q: each row resumes from
 // that state (reference = the local log2-sum-exp, l = 1, accumulator = the
 // local output, the bf16 value plus its residual) and continues over the
 // first n_I tiles of L_t, then overwrites its row of O, so the output is
@@ -102,6 +103,10 @@ constexpr float kRescaleSum = 256.0f;
 // Rows whose logits provably stay below reference + kSafeSpan (log2 units)
 // skip the per-tile row maximum: no p can overflow fp32 before the rescale.
 constexpr float kSafeSpan = 120.0f;
+// The local pass hands each half-row to the sparse pass as bf16 values plus
+// bf16 residuals; the residuals are stored and read only when one of the 64
+// bf16 values reaches this magnitude.
+constexpr float kResidualFrom = 1.0f;
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -561,22 +566,34 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_fwd(AttnArgs a) {
     for (int db = 0; db < 4; ++db) oacc[db] = f32x16{};
   } else {
     const size_t ro = (bh * a.N + iq) * kHeadDim;
+    float amax = 0.f;  // largest |value| of the lane's 64 bf16 values
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         const size_t e = ro + db * 32 + 8 * g4 + 4 * lh;
         const uint2 w = *reinterpret_cast<const uint2*>(a.o + e);
-        const uint2 r = *reinterpret_cast<const uint2*>(a.olo + e);
-        oacc[db][4 * g4 + 0] =
-            __uint_as_float(w.x << 16) + __uint_as_float(r.x << 16);
-        oacc[db][4 * g4 + 1] = __uint_as_float(w.x & 0xffff0000u) +
-                               __uint_as_float(r.x & 0xffff0000u);
-        oacc[db][4 * g4 + 2] =
-            __uint_as_float(w.y << 16) + __uint_as_float(r.y << 16);
-        oacc[db][4 * g4 + 3] = __uint_as_float(w.y & 0xffff0000u) +
-                               __uint_as_float(r.y & 0xffff0000u);
+        oacc[db][4 * g4 + 0] = __uint_as_float(w.x << 16);
+        oacc[db][4 * g4 + 1] = __uint_as_float(w.x & 0xffff0000u);
+        oacc[db][4 * g4 + 2] = __uint_as_float(w.y << 16);
+        oacc[db][4 * g4 + 3] = __uint_as_float(w.y & 0xffff0000u);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          amax = fmaxf(amax, fabsf(oacc[db][4 * g4 + j]));
       }
+    if (amax >= kResidualFrom) {  // the local pass stored the residuals
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const uint2 r = *reinterpret_cast<const uint2*>(
+              a.olo + ro + db * 32 + 8 * g4 + 4 * lh);
+          oacc[db][4 * g4 + 0] += __uint_as_float(r.x << 16);
+          oacc[db][4 * g4 + 1] += __uint_as_float(r.x & 0xffff0000u);
+          oacc[db][4 * g4 + 2] += __uint_as_float(r.y << 16);
+          oacc[db][4 * g4 + 3] += __uint_as_float(r.y & 0xffff0000u);
+        }
+    }
     m = a.lse2[bh * a.N + iq];
     l = 1.f;
   }
@@ -746,6 +763,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_fwd(AttnArgs a) {
   const float ln2 = 0.69314718055994530942f;
   const float inv = 1.f / l;
   const size_t ro = (bh * a.N + iq) * kHeadDim;
+  uint2 res[16];     // local pass: the residuals of the lane's 64 values
+  float amax = 0.f;  // and the largest |bf16 value| among them
 #pragma unroll
   for (int db = 0; db < 4; ++db)
 #pragma unroll
@@ -756,13 +775,26 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_fwd(AttnArgs a) {
       for (int j = 0; j < 4; ++j) {
         const float y = oacc[db][4 * g4 + j] * inv;
         v4[j] = (__bf16)y;
-        if (kLoc) r4[j] = (__bf16)(y - (float)v4[j]);  // exact difference
+        if (kLoc) {
+          r4[j] = (__bf16)(y - (float)v4[j]);  // exact difference
+          amax = fmaxf(amax, fabsf((float)v4[j]));
+        }
       }
       *reinterpret_cast<uint2*>(a.o + ro + d0) = __builtin_bit_cast(uint2, v4);
-      if (kLoc)
-        *reinterpret_cast<uint2*>(a.olo + ro + d0) =
-            __builtin_bit_cast(uint2, r4);
+      if (kLoc) res[4 * db + g4] = __builtin_bit_cast(uint2, r4);
     }
+  // residuals only where they matter: values below kResidualFrom in
+  // magnitude lose at most 2^-9 of it by the rounding to bf16, well inside
+  // the output tolerance; the sparse pass reads them under the same test
+  // on the same bf16 values
+  if (kLoc && amax >= kResidualFrom) {
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4)
+        *reinterpret_cast<uint2*>(a.olo + ro + db * 32 + 8 * g4 + 4 * lh) =
+            res[4 * db + g4];
+  }
   const float lse2v = m + log2f(l);
   if (kLoc && lh == 0) a.lse2[bh * a.N + iq] = lse2v;
   if (a.lse != nullptr && lh == 0) a.lse[bh * a.N + iq] = lse2v * ln2;

@@ -197,6 +197,24 @@ int sparse_attn_forward(const sa_params* p, const void* q, const void* k,
                         size_t workspace_bytes, hipStream_t stream,
                         hipStream_t side_stream, sa_plan** out);
 
+/* For callers that cannot allocate device memory (code under graph
+ * capture, tight serving loops, harnesses that forbid it): the same
+ * results as sparse_attn_forward with side_stream == stream (plan, then
+ * prefill, all on `stream`, which must belong to the current device), with
+ * the workspace taken from a fixed device array of SA_STATIC_SCRATCH_BYTES
+ * that the library holds on each GPU it runs on until the process ends.
+ * No plan object is returned and nothing is allocated (no device memory, no
+ * host memory, no events). Arguments as for sparse_attn_forward; a shape
+ * whose workspace (sparse_attn_workspace_bytes) exceeds
+ * SA_STATIC_SCRATCH_BYTES returns SA_ERR_WORKSPACE_TOO_SMALL before
+ * anything is launched. Every call on one GPU shares that GPU's array:
+ * calls that overlap on one GPU (two streams, two threads) race and give
+ * unspecified results; calls in stream order do not interfere. */
+#define SA_STATIC_SCRATCH_BYTES (256ull << 20)
+int sparse_attn_forward_static(const sa_params* p, const void* q,
+                               const void* k, const void* v, void* o,
+                               float* lse, hipStream_t stream);
+
 /* Change the threshold of an existing plan (the index arrays do not depend
  * on tau). Returns SA_ERR_INVALID_ARG for tau < 0 or NaN. */
 int sparse_attn_plan_set_tau(sa_plan* plan, double tau);

@@ -23,7 +23,8 @@ from . import _lib
 from ._lib import (SA_NO_QPERM, SA_NO_KVPERM, SA_NO_EARLYSTOP,
                    SA_LOCAL_ONLY, SA_SEGMENT_KV, SparseAttnError)
 
-__all__ = ["plan", "prefill", "forward", "SparsePlan", "SA_NO_QPERM",
+__all__ = ["plan", "prefill", "forward", "forward_static", "SparsePlan",
+           "SA_NO_QPERM",
            "SA_NO_KVPERM",
            "SA_NO_EARLYSTOP", "SA_LOCAL_ONLY", "SA_SEGMENT_KV",
            "SparseAttnError",
@@ -293,6 +294,35 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, segment: int,
 
     pl = SparsePlan(q, k, segment, tau, block, flags, stream, _launch=launch)
     return (pl, o, lse) if return_lse else (pl, o)
+
+
+def forward_static(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                   segment: int, tau: float, block: int = 64, flags: int = 0,
+                   out: Optional[torch.Tensor] = None,
+                   lse: Optional[torch.Tensor] = None, stream=None):
+    """Plan and prefill on one stream with the library's fixed device
+    scratch (sparse_attn_forward_static): no workspace and no plan object;
+    the library allocates nothing. Pass `out` (and `lse`) to allocate
+    nothing here either. Shapes whose workspace exceeds
+    SA_STATIC_SCRATCH_BYTES are rejected. Calls that overlap on one GPU
+    race. Returns o, or (o, lse) when lse is given."""
+    lib = _lib.load()
+    for x, n in ((q, "q"), (k, "k"), (v, "v")):
+        _check_tensor(x, n)
+    if k.shape != v.shape:
+        raise ValueError("k and v shapes do not agree")
+    o = out if out is not None else torch.empty_like(q)
+    _check_tensor(o, "out")
+    params = _params(q, k, segment, tau, block, flags)
+    st = lib.sparse_attn_forward_static(
+        ctypes.byref(params), ctypes.c_void_p(q.data_ptr()),
+        ctypes.c_void_p(k.data_ptr()), ctypes.c_void_p(v.data_ptr()),
+        ctypes.c_void_p(o.data_ptr()),
+        ctypes.c_void_p(lse.data_ptr() if lse is not None else 0),
+        ctypes.c_void_p(_stream_ptr(stream)))
+    _lib.check(st, "sparse_attn_forward_static")
+    _record((q, k, v, o, lse), [_stream_of(stream)])
+    return (o, lse) if lse is not None else o
 
 
 def prefill(pl: SparsePlan, q: torch.Tensor, k: torch.Tensor,

@@ -15,6 +15,8 @@ SA_ERR_HIP = -4
 SA_ERR_NULL_POINTER = -5
 SA_ERR_HOST_ALLOC = -6
 
+SA_STATIC_SCRATCH_BYTES = 256 << 20  # scratch of sparse_attn_forward_static
+
 SA_NO_QPERM = 1
 SA_NO_KVPERM = 2
 SA_NO_EARLYSTOP = 4
@@ -33,7 +35,7 @@ SA_EXPORT_TOPK_MASK = 8
 
 EXPORTED_SYMBOLS = (
     "sparse_attn_workspace_bytes", "sparse_attn_plan", "sparse_attn_prefill",
-    "sparse_attn_forward",
+    "sparse_attn_forward", "sparse_attn_forward_static",
     "sparse_attn_plan_set_tau", "sparse_attn_plan_set_budget",
     "sparse_attn_plan_set_max_threshold",
     "sparse_attn_topk_scratch_bytes", "sparse_attn_plan_set_topk",
@@ -82,6 +84,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.sparse_attn_forward.argtypes = [P, vp, vp, vp, vp, vp, vp, sz, vp, vp,
                                         ctypes.POINTER(vp)]
     lib.sparse_attn_forward.restype = i32
+    lib.sparse_attn_forward_static.argtypes = [P, vp, vp, vp, vp, vp, vp]
+    lib.sparse_attn_forward_static.restype = i32
     lib.sparse_attn_plan_set_tau.argtypes = [vp, ctypes.c_double]
     lib.sparse_attn_plan_set_tau.restype = i32
     lib.sparse_attn_plan_set_budget.argtypes = [vp, i32]

@@ -7,6 +7,7 @@
 #include <cstdlib>
 #include <cstring>
 #include <limits>
+#include <mutex>
 #include <new>
 
 #include "sa_launch.h"
@@ -244,6 +245,38 @@ int run_stop_scan(const sa_plan* pl, hipStream_t s) {
 
 }  // namespace
 
+// Scratch of sparse_attn_forward_static, for callers that cannot
+// allocate: one fixed array per GPU, held until the process ends. In host
+// code the array's name is only a stand-in; its device address on the
+// current GPU comes from hipGetSymbolAddress (kept per device, taken on the
+// first call on that device) and is the only form passed to kernels.
+static __device__ __align__(256) unsigned char scratch[SA_STATIC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_addr[kMaxDevices] = {};
+
+// The scratch array's device address on the current device.
+int static_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return SA_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return SA_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch_addr[dev] == nullptr) {
+    void* addr = nullptr;
+    if (hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch)) != hipSuccess ||
+        addr == nullptr)
+      return SA_ERR_HIP;
+    g_scratch_addr[dev] = addr;
+  }
+  *out = g_scratch_addr[dev];
+  return SA_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 size_t sparse_attn_workspace_bytes(const sa_params* p) {
@@ -252,6 +285,17 @@ size_t sparse_attn_workspace_bytes(const sa_params* p) {
 }
 
 namespace {
+
+// A plan object over a workspace (validated by the caller).
+void plan_fill(sa_plan* pl, const sa_params* p, const void* q, const void* k,
+               void* workspace) {
+  pl->p = *p;
+  pl->d = dims_of(p);
+  pl->lay = layout_of(pl->d);
+  pl->ws = static_cast<char*>(workspace);
+  pl->q = q;
+  pl->k = k;
+}
 
 // Validation and the plan object (host only; no launch).
 int plan_create(const sa_params* p, const void* q, const void* k,
@@ -269,12 +313,7 @@ int plan_create(const sa_params* p, const void* q, const void* k,
   if (workspace_bytes < lay.total) return SA_ERR_WORKSPACE_TOO_SMALL;
   sa_plan* pl = new (std::nothrow) sa_plan;
   if (pl == nullptr) return SA_ERR_HOST_ALLOC;
-  pl->p = *p;
-  pl->d = d;
-  pl->lay = lay;
-  pl->ws = static_cast<char*>(workspace);
-  pl->q = q;
-  pl->k = k;
+  plan_fill(pl, p, q, k, workspace);
   *out = pl;
   return SA_OK;
 }
@@ -597,6 +636,31 @@ const char* sparse_attn_status_string(int status) {
     case SA_ERR_HOST_ALLOC: return "host allocation failed";
     default: return "unknown status";
   }
+}
+
+int sparse_attn_forward_static(const sa_params* p, const void* q,
+                               const void* k, const void* v, void* o,
+                               float* lse, hipStream_t stream) {
+  const int st = validate(p);
+  if (st != SA_OK) return st;
+  if (q == nullptr || k == nullptr || v == nullptr || o == nullptr)
+    return SA_ERR_NULL_POINTER;
+  if (layout_of(dims_of(p)).total > SA_STATIC_SCRATCH_BYTES)
+    return SA_ERR_WORKSPACE_TOO_SMALL;
+  void* ws = nullptr;
+  int rc = static_scratch(&ws);
+  if (rc != SA_OK) return rc;
+  // every array of the layout is written before it is read within this
+  // call (the residuals are read only where this call's local pass wrote
+  // them), so nothing carries over from an earlier call
+  sa_plan pl;
+  plan_fill(&pl, p, q, k, ws);
+  rc = plan_launch(&pl, stream);
+  if (rc != SA_OK) return rc;
+  const AttnArgs a = attn_args(&pl, q, k, v, o, lse);
+  rc = hip_status(launch_attention_local(a, stream));
+  if (rc != SA_OK) return rc;
+  return sparse_passes(&pl, a, stream);
 }
 
 }  // extern "C"

@@ -25,7 +25,7 @@ def declared_functions():
 def test_every_declared_symbol_is_exported():
     lib = _lib.load()
     names = declared_functions()
-    assert len(names) == 14
+    assert len(names) == 15
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(_lib.EXPORTED_SYMBOLS)
@@ -95,6 +95,27 @@ def test_forward_rejects_before_launch():
                                    n - 1, None, None, ctypes.byref(out)) == \
         _lib.SA_ERR_WORKSPACE_TOO_SMALL
     assert out.value is None
+
+
+def test_forward_static_rejects_before_launch():
+    """The entry point without allocation rejects null pointers, invalid
+    shapes and shapes whose workspace exceeds its fixed scratch before it
+    touches the GPU."""
+    lib = _lib.load()
+    f = ctypes.c_void_p(1 << 20)
+    p = P()
+    assert ws(p) <= _lib.SA_STATIC_SCRATCH_BYTES
+    call = lambda p_, *a: lib.sparse_attn_forward_static(
+        ctypes.byref(p_) if p_ is not None else None, *a, None, None)
+    assert call(None, f, f, f, f) == _lib.SA_ERR_NULL_POINTER
+    for args in ((None, f, f, f), (f, None, f, f), (f, f, None, f),
+                 (f, f, f, None)):
+        assert call(p, *args) == _lib.SA_ERR_NULL_POINTER
+    assert call(P(segment=100), f, f, f, f) == _lib.SA_ERR_UNSUPPORTED_SHAPE
+    assert call(P(tau=-1.0), f, f, f, f) == _lib.SA_ERR_INVALID_ARG
+    big = P(heads_q=32, heads_kv=8, seq_len=32768, segment=2048)
+    assert ws(big) > _lib.SA_STATIC_SCRATCH_BYTES
+    assert call(big, f, f, f, f) == _lib.SA_ERR_WORKSPACE_TOO_SMALL
 
 
 def test_other_entry_points_reject_null():

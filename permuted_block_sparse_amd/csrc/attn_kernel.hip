@@ -34,14 +34,20 @@
 // helps with the gathers.
 //
 // Pipeline: each wave overlaps its matrix and vector work within a step.
-// LDS holds three K/V tile buffers and each wave two sets of logit
-// registers. Step s: the reference of tile s (see the online softmax
-// below); the QK MFMAs of tile s + 1 interleaved with the exponentials of
-// tile s; the PV MFMAs of tile s; tile s + 2's rows (loaded into registers
-// during step s - 1) into the buffer that held tile s - 1; the loads of
-// tile s + 3's rows and of step s + 4's indices. One barrier per step. A
-// wave whose block is done (or that holds no rows) runs the same
-// instructions as a no-op, so no branch splits the MFMA and VALU work.
+// LDS holds a ring of four K tile buffers and a ring of four V tile buffers
+// (tile j in slot j % 4), each wave two sets of logit registers. Step s:
+// the reference of tile s (see the online softmax below); the QK MFMAs of
+// tile s + 1 interleaved with the exponentials of tile s; the PV MFMAs of
+// tile s; the K rows of tile s + 3 and the V rows of tile s + 2 (loaded
+// into registers during step s - 1) into the slots of tiles s - 1 and
+// s - 2; the loads of the K rows of tile s + 4, the V rows of tile s + 3
+// and the indices of tile s + 5. One barrier per pair of steps (s even,
+// s + 1): the pair reads K slots s + 1, s + 2 and V slots s, s + 1, and
+// writes K slots s + 3, s + 4 and V slots s + 2, s + 3, the four other
+// slots of each ring, so the waves of a workgroup may be a step apart
+// between barriers. A wave whose block is done (or that holds no rows)
+// runs the same instructions as a no-op, so no branch splits the MFMA and
+// VALU work.
 //
 // Exact per-block max mode (the BSFA page's test, instead of the stop): every
 // tile of L_t is scored and attended iff the largest logit of the 64 x 64
@@ -226,6 +232,30 @@ __device__ __forceinline__ void store_rows(char* kdst, char* vdst,
   *reinterpret_cast<uint4*>(vdst + a.v + 2048) = r.v1;
 }
 
+// One lane's 32 bytes of one K or V row (chunks c and 8 + c).
+struct Half {
+  uint4 a, b;
+};
+__device__ __forceinline__ Half load_half(const uint16_t* base, int key,
+                                          int nkeys, int lane) {
+  key = min(max(key, 0), nkeys - 1);
+  const size_t off = (size_t)key * kHeadDim + 8 * (lane & 7);
+  Half r;
+  r.a = *reinterpret_cast<const uint4*>(base + off);
+  r.b = *reinterpret_cast<const uint4*>(base + off + 64);
+  return r;
+}
+__device__ __forceinline__ void store_khalf(char* kdst, const Half& r,
+                                            StoreAddr a) {
+  *reinterpret_cast<uint4*>(kdst + a.k) = r.a;
+  *reinterpret_cast<uint4*>(kdst + a.k + 4096) = r.b;
+}
+__device__ __forceinline__ void store_vhalf(char* vdst, const Half& r,
+                                            StoreAddr a) {
+  *reinterpret_cast<uint4*>(vdst + a.v) = r.a;
+  *reinterpret_cast<uint4*>(vdst + a.v + 2048) = r.b;
+}
+
 // Per-lane read offsets of the swizzled layouts: K block (kb, s) is read at
 // 1024 (8 kb + s) + kofs[s % 4]; V block id (column block db) at
 // 512 id + vofs[db % 2].
@@ -395,8 +425,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_fwd(AttnArgs a) {
   constexpr bool kLoc = kMode == kLocal;
   if ((kMode == kMaxRef || kMode == kTopKMax) && a.wg_flag[blockIdx.x] == 0)
     return;  // done
-  // three K/V tile buffers of 2 x 16 KB
-  __shared__ __attribute__((aligned(1024))) char tiles[3][2 * kTileBytes];
+  // rings of four K and four V tile buffers of 16 KB (tile j in slot j % 4)
+  __shared__ __attribute__((aligned(1024))) char kring[4][kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char vring[4][kTileBytes];
   __shared__ int wave_maxrow[kWaves];
   __shared__ int wave_ntiles[kWaves];
   // exact mode: each wave's maximum of the next tile, by step parity
@@ -456,7 +487,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_fwd(AttnArgs a) {
   // more registers and spills
   const int ndiag_sparse = a.local_steps != 0 ? 1 : 0;
 
-  // The first three tiles' rows are requested before the step count is
+  // The first four tiles' rows are requested before the step count is
   // known (that takes a barrier): the local pass's tiles are the segment's
   // first key blocks, a sparse pass's the first tiles of L_t (indices
   // clamped into L_t; in the first segment, which has no L_t and no sparse
@@ -519,8 +550,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_fwd(AttnArgs a) {
     const int x = kLoc ? 0 : *src;
     return computed ? seg0 + s * kBlock + rg : x;
   };
-  const int key0 = first_key(0), key1 = first_key(1), key2 = first_key(2);
-  int raw = kLoc ? 0 : first_key(3);
+  const int key0 = first_key(0), key1 = first_key(1), key2 = first_key(2),
+            key3 = first_key(3);
+  // indices of the rows step 0 loads: V rows of tile 3, K rows of tile 4
+  int raw_v = kLoc ? 0 : key3;
+  int raw_k = kLoc ? 0 : first_key(4);
 
   const int h = g * a.G + (valid ? e % a.G : 0);
   const int Ib = valid ? e / a.G : 0;  // block index within the segment
@@ -546,7 +580,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_fwd(AttnArgs a) {
   const ReadAddr ra = read_addr(lane);
   const Staged r0 = load_rows(kbase, vbase, key0, a.N, lane);
   const Staged r1 = load_rows(kbase, vbase, key1, a.N, lane);
-  Staged nxt = load_rows(kbase, vbase, key2, a.N, lane);
+  const Staged r2 = load_rows(kbase, vbase, key2, a.N, lane);
+  // staged for step 0's stores: K rows of tile 3, V rows of tile 2
+  Half kst = load_half(kbase, key3, a.N, lane);
+  Half vst = {r2.v0, r2.v1};
 
   // the lane's query row as Q^T B operands, for the whole run
   bf16x8 qr[8];
@@ -634,22 +671,27 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_fwd(AttnArgs a) {
   auto key_of = [&](int s, int row, int raw) {
     return s < ndiag ? seg0 + s * kBlock + row : raw;
   };
-  auto stage = [&](int s, int raw) {
-    return load_rows(kbase, vbase, key_of(s, rg, raw), a.N, lane);
-  };
 
-  // Software pipeline, one step per tile s: the QK of tile s + 1 (buffer
-  // (s + 1) % 3) is issued between the row rescale and the exponentials of
-  // tile s, then the PV of tile s (buffer s % 3), then tile s + 2's rows
-  // (loaded during step s - 1) go to buffer (s + 2) % 3, which held tile
-  // s - 1, and the loads of tile s + 3's rows and tile s + 4's indices are
-  // issued. One barrier per step. A wave whose block has stopped (or whose
-  // tile the exact test rejects) runs the same instructions as a no-op.
-  store_rows(tiles[0], tiles[0] + kTileBytes, r0, sta);
-  store_rows(tiles[1], tiles[1] + kTileBytes, r1, sta);
+  // Software pipeline, one step per tile s: the QK of tile s + 1 (K slot
+  // (s + 1) % 4) is issued between the row rescale and the exponentials of
+  // tile s, then the PV of tile s (V slot s % 4), then the staged K rows of
+  // tile s + 3 and V rows of tile s + 2 go to their slots and the next rows
+  // and indices are loaded. A barrier after every odd step (after every
+  // step in the exact mode, whose maxima travel through LDS from one step
+  // to the next). A wave whose block has stopped (or whose tile the exact
+  // test rejects) runs the same instructions as a no-op. Before the first
+  // step: K and V of tiles 0 and 1 and K of tile 2 in LDS, K of tile 3 and
+  // V of tile 2 staged.
+  store_rows(kring[0], vring[0], r0, sta);
+  store_rows(kring[1], vring[1], r1, sta);
+  store_khalf(kring[2], Half{r2.k0, r2.k1}, sta);
   __syncthreads();
   f32x16 sa[2], sb[2];
-  qk_tile(tiles[0], qr, sa, ra);
+  qk_tile(kring[0], qr, sa, ra);
+  // the first pair of steps refills the slot of tile 0: every wave must have
+  // read it (the bounded-row test and the exact mode's maxima end in a
+  // barrier of their own)
+  if (!kFast && !kExact) __syncthreads();
   // causal mask of local step s: key j0 + off of the tile is masked iff
   // off > iq - j0 - 4 lh
   auto mask_local = [&](int s, f32x16 (&cur)[2]) {
@@ -693,7 +735,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_fwd(AttnArgs a) {
     }
   }
   int n_visit = 0;     // exact mode: tiles attended
-  auto body = [&](int s, f32x16 (&cur)[2], f32x16 (&nxs)[2]) {
+  auto body = [&](int s, f32x16 (&cur)[2], f32x16 (&nxs)[2], bool bar) {
     const bool local = s < ndiag;  // every step of the local pass
     // the local pass: block Ib sees key blocks 0 .. Ib, the last one masked
     if (kLoc && s == Ib) mask_local(s, cur);
@@ -710,12 +752,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_fwd(AttnArgs a) {
     }
     if (kExact && !act) {
       // a tile the exact test rejects (most of them): only the next QK
-      qk_tile(tiles[(s + 1) % 3], qr, nxs, ra);
+      qk_tile(kring[(s + 1) & 3], qr, nxs, ra);
     } else {
       const float muse = kFast ? (act ? m : INFINITY)
                                : row_rescale(cur, oacc, m, l, a.c2, act);
       __builtin_amdgcn_sched_barrier(0);
-      float rs = qk_exp(tiles[(s + 1) % 3], qr, nxs, cur, a.c2, muse, ra);
+      float rs = qk_exp(kring[(s + 1) & 3], qr, nxs, cur, a.c2, muse, ra);
       if (kFast && __builtin_amdgcn_ballot_w64(rs > kRescaleSum) != 0) {
         // rare: a p value may exceed 2^8; divide the row by its largest p
         // (this raises the reference by log2 of it)
@@ -733,7 +775,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_fwd(AttnArgs a) {
       }
       l += sum_xor32(rs);
       __builtin_amdgcn_sched_barrier(0);
-      pv_tile(tiles[s % 3] + kTileBytes, cur, oacc, ra);
+      pv_tile(vring[s & 3], cur, oacc, ra);
     }
     if (kExact) {
       // this half's maximum of tile s + 1, for the other half (the slot of
@@ -741,19 +783,27 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_fwd(AttnArgs a) {
       my_max = wave_max(lane_max(nxs));
       if (lane == 0) tile_max[(s + 1) & 1][wave] = __float_as_uint(my_max);
     }
-    char* const nb = tiles[(s + 2) % 3];
-    store_rows(nb, nb + kTileBytes, nxt, sta);
-    nxt = stage(s + 3, raw);
-    if (!kLoc) raw = *key_src(s + 4, rg);
-    wait_lgkm0();
-    __builtin_amdgcn_s_barrier();
+    // K rows of tile s + 3 and V rows of tile s + 2 (loaded during step
+    // s - 1) into the slots of tiles s - 1 and s - 2, then the loads of the
+    // K rows of tile s + 4, the V rows of tile s + 3 and the index of tile
+    // s + 5
+    store_khalf(kring[(s + 3) & 3], kst, sta);
+    store_vhalf(vring[(s + 2) & 3], vst, sta);
+    vst = load_half(vbase, key_of(s + 3, rg, raw_v), a.N, lane);
+    kst = load_half(kbase, key_of(s + 4, rg, raw_k), a.N, lane);
+    raw_v = raw_k;
+    if (!kLoc) raw_k = *key_src(s + 5, rg);
+    if (bar) {
+      wait_lgkm0();
+      __builtin_amdgcn_s_barrier();
+    }
   };
   int s = 0;
   for (; s + 1 < nsteps; s += 2) {
-    body(s, sa, sb);
-    body(s + 1, sb, sa);
+    body(s, sa, sb, kExact);
+    body(s + 1, sb, sa, true);
   }
-  if (s < nsteps) body(s, sa, sb);
+  if (s < nsteps) body(s, sa, sb, false);
   __builtin_amdgcn_s_waitcnt(0);  // index loads of steps never taken
 
   // ---- epilogue: normalise, round to bf16, scatter to the original rows

@@ -438,6 +438,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_fwd(AttnArgs a) {
   __shared__ uint32_t tk_words[4][kMaskWords];
   __shared__ int tk_step[kMaxTiles];
   __shared__ int tk_count;
+  __shared__ int pool_claim;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int lq = lane & 31, lh = lane >> 5;
   const int qsub = wave & 3, half = wave >> 2;
@@ -446,7 +447,29 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_fwd(AttnArgs a) {
   // Groups are ranked by descending t (longest work first). Consecutive
   // workgroup ids are dispatched round-robin over the 8 XCDs; group q runs on
   // XCD q % 8 so that all workgroups of one group share that XCD's L2.
-  const int p = blockIdx.x;
+  // Tail pool of the bounded-reference launch: the XCDs' shares of the work
+  // differ (each holds the groups of its own KV heads, whose stop points
+  // differ, and the XCDs do not run at quite the same speed), so the last
+  // groups of every XCD's list go to a pool. A workgroup of a pool slot,
+  // and each of the extra workgroups launched after the grid, claims the
+  // next job of the pool (whole groups in list order, so a group's
+  // workgroups mostly run together on one XCD and share its L2); the XCDs
+  // that reach their pool slots first take more of it, and a workgroup
+  // that finds the pool empty exits. The job (p) is then that slot.
+  int p = blockIdx.x;
+  if (kMode == kFastRef && a.pool_start >= 0 && (p >> 3) >= a.pool_start) {
+    if (tid == 0) pool_claim = atomicAdd(a.pool_ctr, 1);
+    __syncthreads();
+    const int c = pool_claim;
+    const int slots = (a.n_groups >> 3) * a.wg_per_group;
+    if (c >= 8 * (slots - a.pool_start)) return;  // the pool is empty
+    const int q = c / a.wg_per_group, ch = c % a.wg_per_group;
+    p = (q & 7) +
+        8 * ((a.pool_start / a.wg_per_group + (q >> 3)) * a.wg_per_group + ch);
+  }
+  // the local pass precedes every sparse pass: it clears the pool counter
+  if (kLoc && blockIdx.x == 0 && tid == 0 && a.pool_ctr != nullptr)
+    *a.pool_ctr = 0;
   int grp, chunk;
   if ((a.n_groups & 7) == 0) {
     const int x = p & 7, slot = p >> 3;
@@ -652,7 +675,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_fwd(AttnArgs a) {
   const int nsteps = ndiag + ntiles;
   if (!kLoc && ntiles == 0) {
     // no sparse tile: the local pass's output and lse are final
-    if (kFast && tid == 0) a.wg_flag[blockIdx.x] = 0;
+    if (kFast && tid == 0) a.wg_flag[p] = 0;
     if (kExact && valid && lane == 0 && half == 0) *nI_ptr = 0;
     __builtin_amdgcn_s_waitcnt(0);  // the first tiles' loads
     return;
@@ -728,7 +751,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_fwd(AttnArgs a) {
     const float bound = sqrtf(qn * a.kmax2[bg]) * a.c2 * (1.f + 1.f / 1024.f);
     const bool safe = bound - m <= kSafeSpan;  // false for NaN
     const int unsafe = __syncthreads_or(valid && !safe);
-    if (tid == 0) a.wg_flag[blockIdx.x] = unsafe;
+    if (tid == 0) a.wg_flag[p] = unsafe;
     if (unsafe) {
       __builtin_amdgcn_s_waitcnt(0);  // loads issued by the prologue
       return;
@@ -876,6 +899,18 @@ __global__ __launch_bounds__(256) void k_v_to_f16(const uint4* __restrict__ v,
 
 int attention_blocks_per_wg() { return 4; }
 
+void set_tail_pool(AttnArgs& a) {
+  // the last 8 groups of each XCD's list (at most all of them), with up to
+  // half as many extra workgroups per XCD as it has pool slots
+  a.pool_start = -1;
+  a.pool_extra = 0;
+  if ((a.n_groups & 7) != 0 || a.n_groups < 8) return;
+  const int per_xcd = a.n_groups >> 3;
+  const int pg = per_xcd < 8 ? per_xcd : 8;
+  a.pool_start = (per_xcd - pg) * a.wg_per_group;
+  a.pool_extra = pg * a.wg_per_group / 2;
+}
+
 hipError_t launch_attention_local(const AttnArgs& a, hipStream_t s) {
   const long long n8 = (long long)a.B * a.Hkv * a.N * (kHeadDim / 8);
   hipLaunchKernelGGL(k_v_to_f16, dim3((unsigned)((n8 + 255) / 256)),
@@ -908,8 +943,10 @@ hipError_t launch_attention_sparse(const AttnArgs& a, hipStream_t s) {
     return hipGetLastError();
   }
   // the bounded workgroups, then (flagged by the first launch) the others
-  hipLaunchKernelGGL(k_attn_fwd<kFastRef>, dim3(total), dim3(kThreads), 0, s,
-                     a);
+  const int fast_total =
+      total + (a.pool_start >= 0 ? 8 * a.pool_extra : 0);
+  hipLaunchKernelGGL(k_attn_fwd<kFastRef>, dim3(fast_total), dim3(kThreads),
+                     0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_attn_fwd<kMaxRef>, dim3(total), dim3(kThreads), 0, s,

@@ -122,7 +122,15 @@ struct AttnArgs {
   int n_groups;
   float c2;        // kappa * log2(e)
   const float* kmax2;  // per (b, KV head): the largest |k_j|^2 (fp32)
-  int32_t* wg_flag;    // per workgroup: 1 = logits unbounded (kMaxRef runs it)
+  int32_t* wg_flag;    // per job: 1 = logits unbounded (kMaxRef runs it)
+  // Tail pool of the bounded-reference launch (a per-XCD rebalancing of
+  // the last groups): slots (per XCD, as in the launch's XCD mapping) from
+  // pool_start on are claimed in group order from *pool_ctr, which the
+  // local pass clears; pool_extra more workgroups per XCD may claim them.
+  // pool_start < 0: no pool.
+  int* pool_ctr;
+  int pool_start;
+  int pool_extra;
   float* lse2;         // per row: the local pass's log2-sum-exp (exp2 domain)
   uint16_t* olo;       // per row: the local output's residual below its bf16
                        // value in O ([B, Hq, N, 128] bf16)
@@ -141,5 +149,7 @@ hipError_t launch_attention_local(const AttnArgs& a, hipStream_t s);
 hipError_t launch_attention_sparse(const AttnArgs& a, hipStream_t s);
 // Query blocks one attention workgroup processes (sets wg_per_group).
 int attention_blocks_per_wg();
+// The tail pool's settings for the launch shape in `a`.
+void set_tail_pool(AttnArgs& a);
 
 }  // namespace sa

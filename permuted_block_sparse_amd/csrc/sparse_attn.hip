@@ -26,7 +26,7 @@ struct Layout {
   size_t pool_part, pooled, vscore, blocksum, segsum, contrast, u;
   size_t key_a, idx_a, key_b, idx_b;
   size_t pi_k, L, pi_q, n_I, rcnt, rcum, qsum, kpart, kmax2, wg_flag, lse2,
-      border, olo, v16, tmask;
+      border, olo, v16, tmask, pool;
   size_t total;
 };
 
@@ -113,6 +113,7 @@ Layout layout_of(const PlanDims& d) {
   L.olo = take(nbh * d.N * kHeadDim * sizeof(uint16_t));
   L.v16 = take(nbg * d.N * kHeadDim * sizeof(uint16_t));
   L.tmask = take(nbh * (d.N / kBlock) * kMaskWords * sizeof(uint32_t));
+  L.pool = take(sizeof(int32_t));
   L.total = off;
   return L;
 }
@@ -408,6 +409,8 @@ AttnArgs attn_args(const sa_plan* plan, const void* q, const void* k,
   a.border = (!a.exact && !a.topk && block_order_used(d))
                  ? plan->at<int32_t>(plan->lay.border)
                  : nullptr;
+  a.pool_ctr = plan->at<int>(plan->lay.pool);
+  set_tail_pool(a);
   return a;
 }
 

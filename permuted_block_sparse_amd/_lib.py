@@ -4,8 +4,10 @@ from __future__ import annotations
 import ctypes
 import os
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib",
-                        "libsparse_attn.so")
+# SPARSE_ATTN_LIB names another build of the library (the tests' sanitized
+# host build); by default the in-tree one
+LIB_PATH = os.environ.get("SPARSE_ATTN_LIB") or os.path.join(
+    os.path.dirname(os.path.abspath(__file__)), "lib", "libsparse_attn.so")
 
 SA_OK = 0
 SA_ERR_INVALID_ARG = -1

@@ -17,12 +17,16 @@
 //   k_stop_scan  : per (b, KV head, segment) and up to 128 query blocks, the
 //                  local-window estimate, then the tiles of L_t in visiting
 //                  order, 32 at a time: key sums of the tiles (gathered rows,
-//                  fp32) in LDS, each block's mean logit, estimate, share
-//                  test in float64; stops once every block has stopped.
+//                  fp32) in LDS, the mean logits of every block against the
+//                  32 tiles as one [128 x 128] x [128 x 32] product on the
+//                  matrix cores (v_mfma_f64_16x16x4f64), then per block the
+//                  estimates and the share test in float64; stops once every
+//                  block has stopped.
 //
 // Arithmetic (shared with nothing else): a tile's mean logit is
 // (qsum . ksum) * kappa / 4096 with both sums in fp32 over bf16 inputs and
-// their dot product summed in float64 (products rounded to fp32). The share E_k / (Acc + E_k) does not depend
+// their dot product in float64 (each product of two fp32 values is exact in
+// float64; the matrix core sums them in float64). The share E_k / (Acc + E_k) does not depend
 // on a common factor of the estimates, so every estimate is taken relative
 // to a running reference, the largest mean logit seen so far (the running
 // total is rescaled when it rises): exp2 of a non-positive argument in fp32,
@@ -38,6 +42,9 @@ namespace sa {
 constexpr int kScanBlocks = 128;  // query blocks per scan workgroup
 constexpr int kScanThreads = 4 * kScanBlocks;
 constexpr int kScanTiles = 32;    // tiles whose key sums sit in LDS at once
+constexpr int kSumStride = 132;   // LDS row stride (floats) of the key sums
+constexpr int kLogitStride = 33;  // LDS row stride (doubles) of the logits
+typedef double f64x4 __attribute__((ext_vector_type(4)));
 
 // Adds the 8 bfloat16 of one 16-byte load to s[0..7].
 static __device__ __forceinline__ void add_bf16x8(float (&s)[8], uint4 w) {
@@ -82,33 +89,7 @@ static __device__ __forceinline__ void sum_rows64(const uint16_t* base,
   }
 }
 
-// Sum over the four lanes of an aligned quad (DPP quad permutations); the
-// two additions pair equal operands, so all four lanes end with equal bits.
-static __device__ __forceinline__ float quad_sum(float x) {
-  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF,
-                                               0xF, true));  // [1,0,3,2]
-  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF,
-                                               0xF, true));  // [2,3,0,1]
-  return x;
-}
-static __device__ __forceinline__ double quad_sum_f64(double x) {
-  auto dpp = [](double v, int ctrl) {
-    const uint64_t u = __double_as_longlong(v);
-    int lo = (int)(uint32_t)u, hi = (int)(uint32_t)(u >> 32);
-    if (ctrl == 0xB1) {
-      lo = __builtin_amdgcn_mov_dpp(lo, 0xB1, 0xF, 0xF, true);
-      hi = __builtin_amdgcn_mov_dpp(hi, 0xB1, 0xF, 0xF, true);
-    } else {
-      lo = __builtin_amdgcn_mov_dpp(lo, 0x4E, 0xF, 0xF, true);
-      hi = __builtin_amdgcn_mov_dpp(hi, 0x4E, 0xF, 0xF, true);
-    }
-    return __longlong_as_double(
-        (long long)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo));
-  };
-  x += dpp(x, 0xB1);  // [1,0,3,2]
-  x += dpp(x, 0x4E);  // [2,3,0,1]
-  return x;
-}
+// Sum over the four lanes of an aligned quad (DPP quad permutations).
 static __device__ __forceinline__ int quad_sum_int(int x) {
   x += __builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, true);
   x += __builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, true);
@@ -139,8 +120,13 @@ __global__ __launch_bounds__(256) void k_block_qsum(
 // Stop points of up to 128 query blocks of one (b, KV head g, segment t).
 // Thread 4 j + dq serves block slot j and dims 32 dq .. + 31 (and rows
 // 16 dq .. + 15 of the block for the visible-pair counts).
-__global__ __launch_bounds__(kScanThreads) void k_stop_scan(StopArgs a) {
-  __shared__ __attribute__((aligned(16))) float ksum[kScanTiles][kHeadDim];
+// Two workgroups per CU (4 waves per SIMD, at most 128 registers): the scan
+// waits on its gathers, and the second workgroup's hide them better than
+// the registers the matrix-core operands would keep without the bound.
+__global__ __launch_bounds__(kScanThreads, 4) void k_stop_scan(StopArgs a) {
+  __shared__ __attribute__((aligned(16))) float ksum[kScanTiles][kSumStride];
+  // mean logits (log2 units) of the chunk: block slot x tile
+  __shared__ double xl[kScanBlocks][kLogitStride];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int j = tid >> 2, dq = tid & 3;
   const int bps = a.S / kBlock;
@@ -166,18 +152,21 @@ __global__ __launch_bounds__(kScanThreads) void k_stop_scan(StopArgs a) {
     return;
   }
 
-  // this thread's quarter of the block's query sum, and its 16 rows
-  // (offsets from the segment start)
-  float qv[32];
+  // the wave's A operands of the logit product for the whole run: lane l
+  // holds block slot 16 w + l % 16, dims 4 s + l / 16 (s = 0..31) of its
+  // query sum (0 for slots past the group)
+  float aq[32];
   {
-    const float4* src = reinterpret_cast<const float4*>(
-        a.qsum + (bh * (a.N / kBlock) + I) * kHeadDim + 32 * dq);
+    const int ja = 16 * wave + (lane & 15);
+    const int ea = chunk * kScanBlocks + ja;
+    const bool va = ea < per_group;
+    const int ha = g * a.G + (va ? ea % a.G : 0);
+    const int Ia = t * bps + (va ? ea / a.G : 0);
+    const float* src = a.qsum +
+                       (((long long)b * a.Hq + ha) * (a.N / kBlock) + Ia) *
+                           kHeadDim + (lane >> 4);
 #pragma unroll
-    for (int x = 0; x < 8; ++x) {
-      const float4 f = src[x];
-      qv[4 * x] = f.x; qv[4 * x + 1] = f.y;
-      qv[4 * x + 2] = f.z; qv[4 * x + 3] = f.w;
-    }
+    for (int s = 0; s < 32; ++s) aq[s] = va ? src[4 * s] : 0.f;
   }
   const int seg0 = t * a.S;
   const int32_t* pq = a.pi_q + bh * a.N + (long long)I * kBlock + 16 * dq;
@@ -205,23 +194,32 @@ __global__ __launch_bounds__(kScanThreads) void k_stop_scan(StopArgs a) {
       }
     }
   };
-  // this quad's mean logit of tile kk in LDS, in log2 units:
-  // (qsum . ksum) kappa log2(e) / 4096; each product rounded once to fp32,
-  // the sum of the 128 products in float64 (its error does not grow with
-  // the partial sums, whatever the size of the logits)
-  auto tile_x = [&](int kk) {
-    const float4* src = reinterpret_cast<const float4*>(&ksum[kk][32 * dq]);
-    double d = 0.0;
-#pragma unroll
-    for (int x = 0; x < 8; ++x) {
-      const float4 f = src[x];
-      d += (double)(qv[4 * x] * f.x);
-      d += (double)(qv[4 * x + 1] * f.y);
-      d += (double)(qv[4 * x + 2] * f.z);
-      d += (double)(qv[4 * x + 3] * f.w);
+  // the mean logits of the 128 block slots against the 32 tiles in LDS, in
+  // log2 units: (qsum . ksum) kappa log2(e) / 4096, the products exact in
+  // float64 and summed in float64 (no error that grows with the size of the
+  // logits). Wave w: slots 16 w .. + 15, two 16 x 16 output tiles, 32
+  // k-steps of 4 dims; B operands: lane l holds tile 16 c + l % 16, dims
+  // 4 s + l / 16. Item r of lane l is slot 16 w + 4 r + l / 16, tile
+  // 16 c + l % 16 (the instruction's output layout). Every wave runs it.
+  auto chunk_logits = [&]() {
+    f64x4 acc0 = {0.0, 0.0, 0.0, 0.0}, acc1 = {0.0, 0.0, 0.0, 0.0};
+    const float* b0 = &ksum[lane & 15][lane >> 4];
+    const float* b1 = &ksum[16 + (lane & 15)][lane >> 4];
+#pragma unroll 8
+    for (int s = 0; s < 32; ++s) {
+      const double av = (double)aq[s];
+      acc0 = __builtin_amdgcn_mfma_f64_16x16x4f64(av, (double)b0[4 * s], acc0,
+                                                  0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f64_16x16x4f64(av, (double)b1[4 * s], acc1,
+                                                  0, 0, 0);
     }
-    return quad_sum_f64(d) * c2k;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      xl[16 * wave + 4 * r + (lane >> 4)][lane & 15] = acc0[r] * c2k;
+      xl[16 * wave + 4 * r + (lane >> 4)][16 + (lane & 15)] = acc1[r] * c2k;
+    }
   };
+  auto tile_x = [&](int kk) { return xl[j][kk]; };
   // estimates relative to the running reference ref (the largest mean
   // logit so far): exp2(x - ref) after raising ref to x if needed, with the
   // running total acc (relative to ref as well) rescaled then
@@ -241,6 +239,8 @@ __global__ __launch_bounds__(kScanThreads) void k_stop_scan(StopArgs a) {
     const int cnt = min(kScanTiles, bps - c0);
     __syncthreads();
     load_sums(true, c0, cnt);
+    __syncthreads();
+    chunk_logits();
     __syncthreads();
     if (valid) {
       // this thread's 16 rows (offsets from the segment start)
@@ -270,6 +270,8 @@ __global__ __launch_bounds__(kScanThreads) void k_stop_scan(StopArgs a) {
     if (!__syncthreads_or(active)) break;
     const int cnt = min(kScanTiles, ntl - k0);
     load_sums(false, k0, cnt);
+    __syncthreads();
+    chunk_logits();
     __syncthreads();
     if (active) {
       for (int kk = 0; kk < cnt; ++kk) {

@@ -31,7 +31,10 @@
 // both halves of a block sit on the same SIMD. K and V tiles are gathered
 // into LDS once per workgroup and read by all 8 waves; the workgroup runs to
 // the largest step count of its blocks, and a wave whose block is done only
-// helps with the gathers.
+// helps with the gathers. Where the shape allows, the local pass gives each
+// workgroup two blocks of the same heads one after the other, blocks i and
+// S / 64 - 1 - i of a segment (S / 64 + 1 steps for every workgroup, half
+// as many workgroups and their fixed costs).
 //
 // Pipeline: each wave overlaps its matrix and vector work within a step.
 // LDS holds a ring of four K tile buffers and a ring of four V tile buffers
@@ -414,7 +417,7 @@ __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F
 // for kMaxRef / kFastRef.
 enum : int {
   kMaxRef = 0, kFastRef = 1, kExactMax = 2, kLocal = 3, kTopKMax = 4,
-  kTopKFast = 5
+  kTopKFast = 5, kLocalPair = 6
 };
 
 template <int kMode>
@@ -422,7 +425,13 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_fwd(AttnArgs a) {
   constexpr bool kExact = kMode == kExactMax;
   constexpr bool kTopK = kMode == kTopKMax || kMode == kTopKFast;
   constexpr bool kFast = kMode == kFastRef || kMode == kTopKFast;
-  constexpr bool kLoc = kMode == kLocal;
+  // kLocalPair: the local pass with two query blocks per workgroup, one
+  // after the other: block i and block S / 64 - 1 - i of the same four heads
+  // (S / 64 + 1 steps in all, the same for every workgroup); the key tiles
+  // run on through both, and at the switch the first block's result is
+  // written and the second block's queries are loaded
+  constexpr bool kPair = kMode == kLocalPair;
+  constexpr bool kLoc = kMode == kLocal || kPair;
   if ((kMode == kMaxRef || kMode == kTopKMax) && a.wg_flag[blockIdx.x] == 0)
     return;  // done
   // rings of four K and four V tile buffers of 16 KB (tile j in slot j % 4)
@@ -480,8 +489,17 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_fwd(AttnArgs a) {
     chunk = p % a.wg_per_group;
   }
   // local pass: the blocks nearest the segment's end (the most key tiles)
-  // first
-  if (kLoc) chunk = a.wg_per_group - 1 - chunk;
+  // first; pairs: the workgroup's head quad and pair index pr give the
+  // first block (S / 64 - 1 - pr, in the numbering of the one-block pass)
+  // and the second (pr)
+  int IbB = 0;
+  if (kPair) {
+    const int hq4 = a.G / 4, pr = chunk / hq4;
+    IbB = pr;
+    chunk = (a.S / kBlock - 1 - pr) * hq4 + chunk % hq4;
+  } else if (kLoc) {
+    chunk = a.wg_per_group - 1 - chunk;
+  }
   const int BH = a.B * a.Hkv;
   const int t = a.T - 1 - grp / BH;
   const int bg = grp % BH, b = bg / a.Hkv, g = bg % a.Hkv;
@@ -565,13 +583,19 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_fwd(AttnArgs a) {
   auto tk_position = [&](int s) -> int {
     return min(tk_entry(s) & 0xffff, max(ntl - 1, 0));
   };
+  // local pass: the key block of step s (pairs: the second block's steps
+  // start over at key block 0)
+  const int IbA = kPair ? (chunk * 4) / a.G : 0;
+  auto loc_block = [&](int s) {
+    return kPair ? (s <= IbA ? s : s - IbA - 1) : s;
+  };
   auto first_key = [&](int s) -> int {
     const bool computed = kLoc || s < ndiag_sparse || ntl == 0;
     const int k = kTopK ? tk_position(s)
                         : min(max(s - ndiag_sparse, 0), max(ntl - 1, 0));
     const int32_t* src = ntl == 0 ? a.pi_q + rg : Lt + (size_t)k * kBlock + rg;
     const int x = kLoc ? 0 : *src;
-    return computed ? seg0 + s * kBlock + rg : x;
+    return computed ? seg0 + loc_block(s) * kBlock + rg : x;
   };
   const int key0 = first_key(0), key1 = first_key(1), key2 = first_key(2),
             key3 = first_key(3);
@@ -596,6 +620,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_fwd(AttnArgs a) {
   // the sparse passes the rows of block I of pi_Q
   const int iq = kLoc ? seg0 + Ib * kBlock + 32 * half + lq
                       : min(max(pq[32 * half + lq], 0), a.N - 1);
+  const int iqB = seg0 + IbB * kBlock + 32 * half + lq;  // pairs
   const uint16_t* qh = a.q + bh * a.N * kHeadDim;
   const uint16_t* kbase = a.k + (size_t)bg * a.N * kHeadDim;
   const uint16_t* vbase = a.v + (size_t)bg * a.N * kHeadDim;
@@ -670,8 +695,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_fwd(AttnArgs a) {
     wgmax = max(wgmax, wave_maxrow[w]);
     ntiles = max(ntiles, wave_ntiles[w]);
   }
-  const int ndiag = kLoc ? min(max((wgmax - seg0) / kBlock + 1, 1), bps)
-                         : ndiag_sparse;
+  const int ndiag = kPair  ? bps + 1
+                    : kLoc ? min(max((wgmax - seg0) / kBlock + 1, 1), bps)
+                           : ndiag_sparse;
   const int nsteps = ndiag + ntiles;
   if (!kLoc && ntiles == 0) {
     // no sparse tile: the local pass's output and lse are final
@@ -692,7 +718,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_fwd(AttnArgs a) {
                                       : pq + (row & 63);
   };
   auto key_of = [&](int s, int row, int raw) {
-    return s < ndiag ? seg0 + s * kBlock + row : raw;
+    return s < ndiag ? seg0 + loc_block(s) * kBlock + row : raw;
   };
 
   // Software pipeline, one step per tile s: the QK of tile s + 1 (K slot
@@ -715,10 +741,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_fwd(AttnArgs a) {
   // read it (the bounded-row test and the exact mode's maxima end in a
   // barrier of their own)
   if (!kFast && !kExact) __syncthreads();
-  // causal mask of local step s: key j0 + off of the tile is masked iff
-  // off > iq - j0 - 4 lh
-  auto mask_local = [&](int s, f32x16 (&cur)[2]) {
-    const int lim = iq - (seg0 + s * kBlock) - 4 * lh;
+  // causal mask of a local step over keys j0 ..: key j0 + off of the tile is
+  // masked iff off > iq - j0 - 4 lh (row iqx)
+  auto mask_local = [&](int j0, int iqx, f32x16 (&cur)[2]) {
+    const int lim = iqx - j0 - 4 * lh;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -761,8 +787,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_fwd(AttnArgs a) {
   auto body = [&](int s, f32x16 (&cur)[2], f32x16 (&nxs)[2], bool bar) {
     const bool local = s < ndiag;  // every step of the local pass
     // the local pass: block Ib sees key blocks 0 .. Ib, the last one masked
-    if (kLoc && s == Ib) mask_local(s, cur);
-    bool act = valid && (kLoc    ? s <= Ib
+    // (pairs: the second block's last step is the workgroup's last)
+    if (kLoc && s == Ib) mask_local(seg0 + Ib * kBlock, iq, cur);
+    if (kPair && s == nsteps - 1) mask_local(seg0 + IbB * kBlock, iqB, cur);
+    bool act = valid && (kPair   ? true
+                         : kLoc  ? s <= Ib
                          : kTopK ? ((tk_entry(s) >> (16 + qsub)) & 1) != 0
                                  : (s - ndiag) < nI);
     if (kExact && !local) {
@@ -821,56 +850,91 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_fwd(AttnArgs a) {
       __builtin_amdgcn_s_barrier();
     }
   };
-  int s = 0;
-  for (; s + 1 < nsteps; s += 2) {
-    body(s, sa, sb, kExact);
-    body(s + 1, sb, sa, true);
-  }
-  if (s < nsteps) body(s, sa, sb, false);
-  __builtin_amdgcn_s_waitcnt(0);  // index loads of steps never taken
-
-  // ---- epilogue: normalise, round to bf16, scatter to the original rows
-  // (the local pass also stores each value's residual below its bf16 value,
-  // for the sparse pass to resume from).
-  if (!valid) return;
-  const float ln2 = 0.69314718055994530942f;
-  const float inv = 1.f / l;
-  const size_t ro = (bh * a.N + iq) * kHeadDim;
-  uint2 res[16];     // local pass: the residuals of the lane's 64 values
-  float amax = 0.f;  // and the largest |bf16 value| among them
-#pragma unroll
-  for (int db = 0; db < 4; ++db)
-#pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) {
-      const int d0 = db * 32 + 8 * g4 + 4 * lh;
-      __bf16 v4[4], r4[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float y = oacc[db][4 * g4 + j] * inv;
-        v4[j] = (__bf16)y;
-        if (kLoc) {
-          r4[j] = (__bf16)(y - (float)v4[j]);  // exact difference
-          amax = fmaxf(amax, fabsf((float)v4[j]));
-        }
-      }
-      *reinterpret_cast<uint2*>(a.o + ro + d0) = __builtin_bit_cast(uint2, v4);
-      if (kLoc) res[4 * db + g4] = __builtin_bit_cast(uint2, r4);
-    }
-  // residuals only where they matter: values below kResidualFrom in
-  // magnitude lose at most 2^-9 of it by the rounding to bf16, well inside
-  // the output tolerance; the sparse pass reads them under the same test
-  // on the same bf16 values
-  if (kLoc && amax >= kResidualFrom) {
+  // ---- epilogue of row iqx: normalise, round to bf16, scatter to the
+  // original row (the local pass also stores each value's residual below
+  // its bf16 value, for the sparse pass to resume from).
+  auto finish = [&](int iqx) {
+    const float ln2 = 0.69314718055994530942f;
+    const float inv = 1.f / l;
+    const size_t ro = (bh * a.N + iqx) * kHeadDim;
+    uint2 res[16];     // local pass: the residuals of the lane's 64 values
+    float amax = 0.f;  // and the largest |bf16 value| among them
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4)
-        *reinterpret_cast<uint2*>(a.olo + ro + db * 32 + 8 * g4 + 4 * lh) =
-            res[4 * db + g4];
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d0 = db * 32 + 8 * g4 + 4 * lh;
+        __bf16 v4[4], r4[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float y = oacc[db][4 * g4 + j] * inv;
+          v4[j] = (__bf16)y;
+          if (kLoc) {
+            r4[j] = (__bf16)(y - (float)v4[j]);  // exact difference
+            amax = fmaxf(amax, fabsf((float)v4[j]));
+          }
+        }
+        *reinterpret_cast<uint2*>(a.o + ro + d0) =
+            __builtin_bit_cast(uint2, v4);
+        if (kLoc) res[4 * db + g4] = __builtin_bit_cast(uint2, r4);
+      }
+    // residuals only where they matter: values below kResidualFrom in
+    // magnitude lose at most 2^-9 of it by the rounding to bf16, well inside
+    // the output tolerance; the sparse pass reads them under the same test
+    // on the same bf16 values
+    if (kLoc && amax >= kResidualFrom) {
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4)
+          *reinterpret_cast<uint2*>(a.olo + ro + db * 32 + 8 * g4 + 4 * lh) =
+              res[4 * db + g4];
+    }
+    const float lse2v = m + log2f(l);
+    if (kLoc && lh == 0) a.lse2[bh * a.N + iqx] = lse2v;
+    if (a.lse != nullptr && lh == 0) a.lse[bh * a.N + iqx] = lse2v * ln2;
+  };
+
+  // steps of the first (or only) block
+  const int nfirst = kPair ? IbA + 1 : nsteps;
+  int s = 0;
+  for (; s + 1 < nfirst; s += 2) {
+    body(s, sa, sb, kExact);
+    body(s + 1, sb, sa, true);
   }
-  const float lse2v = m + log2f(l);
-  if (kLoc && lh == 0) a.lse2[bh * a.N + iq] = lse2v;
-  if (a.lse != nullptr && lh == 0) a.lse[bh * a.N + iq] = lse2v * ln2;
+  if (s < nfirst) body(s, sa, sb, false);
+  if constexpr (kPair) {
+    // the switch: the first block's result out, the softmax restarted for
+    // the second block's rows and its first tile's QK recomputed with their
+    // queries (the last step computed it with the first block's); the key
+    // tiles in flight are already the second block's
+    __builtin_amdgcn_s_waitcnt(0);
+    finish(iq);
+#pragma unroll
+    for (int db = 0; db < 4; ++db) oacc[db] = f32x16{};
+    m = -INFINITY;
+    l = 0.f;
+#pragma unroll
+    for (int x = 0; x < 8; ++x)
+      qr[x] = *reinterpret_cast<const bf16x8*>(qh + (size_t)iqB * kHeadDim +
+                                               16 * x + 8 * lh);
+    qk_tile(kring[nfirst & 3], qr, sa, ra);
+    // every wave has read that tile before any refills its slot (the pair
+    // of steps that starts with an even first step of the second block
+    // writes it)
+    __syncthreads();
+    s = nfirst;
+    // a barrier after every odd step, as before the switch
+    for (; s + 1 < nsteps; s += 2) {
+      body(s, sa, sb, (s & 1) != 0);
+      body(s + 1, sb, sa, (s & 1) == 0);
+    }
+    if (s < nsteps) body(s, sa, sb, false);
+  }
+  __builtin_amdgcn_s_waitcnt(0);  // index loads of steps never taken
+
+  if (!valid) return;
+  finish(kPair ? iqB : iq);
   if (kExact && lane == 0 && half == 0) *nI_ptr = n_visit;
 }
 
@@ -919,8 +983,19 @@ hipError_t launch_attention_local(const AttnArgs& a, hipStream_t s) {
                      reinterpret_cast<uint4*>(a.v16), n8);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  // the dense local windows in the rows' own order; two blocks per
+  // workgroup when the four blocks of a workgroup share their heads (G a
+  // multiple of 4) and the blocks of a segment pair up (an even count)
+  const int bps = a.S / kBlock;
+  if (a.G % 4 == 0 && bps % 2 == 0) {
+    AttnArgs ap = a;
+    ap.wg_per_group = a.wg_per_group / 2;
+    const int total = a.n_groups * ap.wg_per_group;
+    hipLaunchKernelGGL(k_attn_fwd<kLocalPair>, dim3(total), dim3(kThreads), 0,
+                       s, ap);
+    return hipGetLastError();
+  }
   const int total = a.n_groups * a.wg_per_group;
-  // the dense local windows in the rows' own order
   hipLaunchKernelGGL(k_attn_fwd<kLocal>, dim3(total), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }

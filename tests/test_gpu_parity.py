@@ -65,6 +65,14 @@ CASES = [
     # 256 blocks over two workgroups and its 64 local blocks over two chunks
     ("g4_s4096_two_scan_chunks", _spec(1, 4, 1, 8192, 39, n_vert=64,
                                        window=128), 4096, (0.02, 0.1), 0),
+    # the local pass with two blocks per workgroup (4 query heads per KV
+    # head): pairs (3, 0) and (2, 1), whose first blocks end after an even
+    # and an odd number of steps, with and without the sparse pass after it
+    ("local_pairs_g4_s256", _spec(1, 8, 2, 1024, 60), 256, (0.02, 0.1), 0),
+    ("local_only_pairs_g4_s256", _spec(1, 8, 2, 1024, 61), 256, (0.0,),
+     O.SA_LOCAL_ONLY),
+    # one pair per segment: (1, 0)
+    ("local_pairs_g4_s128", _spec(1, 4, 1, 512, 62), 128, (0.05,), 0),
 ]
 
 

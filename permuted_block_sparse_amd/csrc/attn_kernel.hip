@@ -397,8 +397,11 @@ __device__ __forceinline__ float qk_exp(const char* Kt, const bf16x8 (&qr)[8],
 // s_waitcnt lgkmcnt(0) (gfx9 encoding; vmcnt and expcnt left unlimited)
 __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
-// Four instances. kLocal: the local pass (every block's dense local window,
-// rows in their own order). kMaxRef and kFastRef: the sparse pass over the
+// Seven instances. kLocal: the local pass (every block's dense local window,
+// rows in their own order); kLocalPair: the same with two blocks per
+// workgroup, one after the other (see the mapping below; used where the four
+// blocks of a workgroup share their heads and a segment's blocks pair up).
+// kMaxRef and kFastRef: the sparse pass over the
 // first n_I tiles of L_t, n_I given (the early stop's stop points or a
 // budget). kFastRef raises the online softmax's reference only when p
 // values grow past 2^8; it runs the workgroups whose logits are provably

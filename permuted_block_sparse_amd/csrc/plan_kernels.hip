@@ -108,6 +108,10 @@ __device__ __forceinline__ int64_t dot8_split(const int32_t (&f)[8],
 // workgroup's largest squared key norm (fp32; their maximum bounds the
 // attention kernel's logits).
 // --------------------------------------------------------------------------
+// One workgroup covers kScoreRows = 16 passes of 16 rows (four 64-row key
+// blocks), the shape of its loop and of its LDS reduction.
+static_assert(kScoreRows == 16 * 16 && kScoreRows == 4 * kBlock,
+              "k_key_score covers 16 passes of 16 rows per workgroup");
 __global__ __launch_bounds__(256) void k_key_score(
     const uint16_t* __restrict__ k, const int64_t* __restrict__ pooled,
     int64_t* __restrict__ vscore, int32_t* __restrict__ blocksum,

@@ -10,7 +10,8 @@ namespace sa {
 constexpr int kHeadDim = 128;        // supported head dimension
 constexpr int kBlock = 64;           // query-block rows and key-tile keys
 constexpr int kPoolRows = 1024;      // rows per pooling workgroup
-constexpr int kScoreRows = 256;      // rows per scoring workgroup
+constexpr int kScoreRows = 256;      // rows per scoring workgroup (k_key_score
+                                     // is written for exactly 256)
 constexpr int kSortChunk = 4096;     // elements sorted in LDS by one workgroup
 constexpr int kRestrictChunk = 4096; // pi_K entries per restriction workgroup
 constexpr int kRestrictSplit = 8;    // restriction workgroups per chunk (t interleaved)

@@ -16,6 +16,12 @@ constexpr int kSortChunk = 4096;     // elements sorted in LDS by one workgroup
 constexpr int kRestrictChunk = 4096; // pi_K entries per restriction workgroup
 constexpr int kRestrictSplit = 8;    // restriction workgroups per chunk (t interleaved)
 constexpr int kMaxTiles = 2048;      // N / 64 at the largest supported N
+// The kernels' thread layouts are written for these values: 16 lanes of 8
+// elements per 128-wide row, 64-row blocks matching the 32 x 32 MFMA tiles,
+// whole per-thread shares of the restriction and Top-K chunks.
+static_assert(kHeadDim == 128 && kBlock == 64, "row and block shapes");
+static_assert(kRestrictChunk % 256 == 0, "restriction chunk per 256 threads");
+static_assert(kMaxTiles % 64 == 0, "Top-K positions per lane");
 
 struct PlanDims {
   int B, Hq, Hkv, N, S, T, G;
@@ -83,6 +89,8 @@ hipError_t launch_stop_scan(const StopArgs& a, hipStream_t s);
 
 // ---- per-block centroid Top-K selection (instead of the tau stop)
 constexpr int kMaskWords = kMaxTiles / 32;  // bitmask words per query block
+// the attention kernel reads a block's mask one word per lane
+static_assert(kMaskWords == 64, "one Top-K mask word per lane of a wave");
 struct TopkArgs {
   const uint16_t* q;
   const uint16_t* k;

@@ -361,6 +361,35 @@ def test_causal_values_and_later_segments():
     assert np.array_equal(base["n_I"][:, :, :12], pert["n_I"][:, :, :12])
 
 
+def test_random_shapes():
+    """Seeded random combinations of batch, heads per KV head (1-8, odd
+    included), segment length (64-512, odd block counts included), segment
+    count, tau and flags, each against the oracle as in test_parity_small."""
+    rng = np.random.default_rng(2026)
+    flagset = [0, 0, 0, O.SA_NO_QPERM, O.SA_NO_KVPERM, O.SA_SEGMENT_KV,
+               O.SA_LOCAL_ONLY, O.SA_NO_EARLYSTOP,
+               O.SA_SEGMENT_KV | O.SA_NO_QPERM]
+    for c in range(24):
+        B = int(rng.choice([1, 1, 2]))
+        Hkv = int(rng.choice([1, 2]))
+        G = int(rng.choice([1, 2, 3, 4, 4, 8]))
+        S = int(rng.choice([64, 128, 192, 256, 320, 512]))
+        T = int(rng.integers(1, 7))
+        while T > 1 and B * G * Hkv * S * T > 6 * 4096:
+            T -= 1
+        N = S * T
+        tau = float(rng.choice([0.0, 0.005, 0.02, 0.1, 0.4]))
+        flags = int(rng.choice(flagset))
+        spec = StripeSpec(B, G * Hkv, Hkv, N, 128, n_vert=min(16, N // 16),
+                          n_horiz=min(8, N // 32), window=min(64, N // 8),
+                          seed=3000 + c)
+        say(f"[random {c}] B={B} Hq={G * Hkv} Hkv={Hkv} N={N} S={S} "
+            f"tau={tau} flags={flags}")
+        q, k, v = make_stripe_inputs(spec)
+        err, mse, nties, g, _, _ = _check_case(q, k, v, S, tau, flags)
+        say(f"   max_abs={err:.3g} mse={mse:.3g} ties={nties}")
+
+
 def test_parity_llama_layer_n32k_full_plan_sampled_outputs():
     """Llama-3.1-8B-shaped layer at N = 32768 (the 32K workload): every index
     array and every stop point against the oracle; outputs on 48 sampled

@@ -171,23 +171,32 @@ def test_forward_matches_plan_then_prefill():
     import torch
     import permuted_block_sparse_amd as pbs
     from tests.gpu_helpers import to_device
-    spec = _spec(1, 4, 1, 4096, 43, n_vert=32, window=128)
-    q, k, v = make_stripe_inputs(spec)
-    tq, tk, tv = to_device(q), to_device(k), to_device(v)
-    S, tau = 512, 0.05
-    pl = pbs.plan(tq, tk, S, tau)
-    o_ref, l_ref = pbs.prefill(pl, tq, tk, tv, return_lse=True)
-    torch.cuda.synchronize()
     side = torch.cuda.Stream()
-    for name, ss in (("side stream", side), ("one stream", None)):
-        say(f"[forward] {name}")
-        pf, o, l = pbs.forward(tq, tk, tv, S, tau, return_lse=True,
-                               side_stream=ss)
+    # the local pass with pairs of blocks (4 query heads per KV head, an
+    # even number of blocks per segment), one block per workgroup (2 heads
+    # per KV head; 3 heads and 5 blocks per segment), a batch of two with
+    # the segment-local KV order
+    shapes = [(_spec(1, 4, 1, 4096, 43, n_vert=32, window=128), 512, 0.05, 0),
+              (_spec(1, 4, 2, 2048, 44), 256, 0.02, 0),
+              (_spec(1, 3, 1, 1600, 45), 320, 0.05, 0),
+              (_spec(2, 8, 2, 1024, 46), 256, 0.1, O.SA_SEGMENT_KV)]
+    for spec, S, tau, flags in shapes:
+        q, k, v = make_stripe_inputs(spec)
+        tq, tk, tv = to_device(q), to_device(k), to_device(v)
+        pl = pbs.plan(tq, tk, S, tau, flags=flags)
+        o_ref, l_ref = pbs.prefill(pl, tq, tk, tv, return_lse=True)
         torch.cuda.synchronize()
-        assert torch.equal(o.view(torch.int16), o_ref.view(torch.int16))
-        assert torch.equal(l, l_ref)
-        for ex in ("pi_k", "pi_q", "restricted_lists", "n_I"):
-            assert np.array_equal(getattr(pf, ex)(), getattr(pl, ex)()), ex
+        for name, ss in (("side stream", side), ("one stream", None)):
+            say(f"[forward] B={spec.batch} Hq={spec.heads_q} "
+                f"Hkv={spec.heads_kv} N={spec.seq_len} S={S} {name}")
+            pf, o, l = pbs.forward(tq, tk, tv, S, tau, flags=flags,
+                                   return_lse=True, side_stream=ss)
+            torch.cuda.synchronize()
+            assert torch.equal(o.view(torch.int16), o_ref.view(torch.int16))
+            assert torch.equal(l, l_ref)
+            for ex in ("pi_k", "pi_q", "restricted_lists", "n_I"):
+                assert np.array_equal(getattr(pf, ex)(),
+                                      getattr(pl, ex)()), ex
     pf.set_tau(0.2)
     pl.set_tau(0.2)
     o2 = pbs.prefill(pf, tq, tk, tv)

@@ -769,3 +769,55 @@ def test_topk_worked_example_and_mode_changes():
     pli = O.plan(q, k, 256, kv_order=np.tile(np.arange(1024), (1, 2, 1)))
     n_i, tr_i = O.stop_points(q, k, pli, 0.05)
     assert not stop_mismatches(p.n_I(), n_i, tr_i, 0.05)
+
+
+def test_random_shapes_selection_modes():
+    """The fixed budget, the exact per-block maximum and the centroid Top-K
+    on seeded random shapes (batch, heads per KV head 1-8, segments of
+    64-512 with odd block counts), four of each, against the oracle."""
+    rng = np.random.default_rng(2027)
+    for c in range(12):
+        B = int(rng.choice([1, 1, 2]))
+        Hkv = int(rng.choice([1, 2]))
+        G = int(rng.choice([1, 2, 3, 4, 4, 8]))
+        S = int(rng.choice([64, 128, 192, 256, 320, 512]))
+        T = int(rng.integers(2, 7))
+        while T > 2 and B * G * Hkv * S * T > 4 * 4096:
+            T -= 1
+        N = S * T
+        spec = StripeSpec(B, G * Hkv, Hkv, N, 128, n_vert=min(16, N // 16),
+                          n_horiz=min(8, N // 32), window=min(64, N // 8),
+                          seed=4000 + c)
+        q, k, v = make_stripe_inputs(spec)
+        pl = O.plan(q, k, S)
+        tag = f"B={B} Hq={G * Hkv} Hkv={Hkv} N={N} S={S}"
+        mode = c % 3
+        if mode == 0:
+            K = int(rng.integers(0, 2 * N // 64))
+            say(f"[random budget] K={K} {tag}")
+            g = run_gpu(q, k, v, S, 0.05, budget=K)
+            n_ref, _ = O.stop_points(q, k, pl, 0.05, budget=K)
+            assert np.array_equal(g["n_I"], n_ref)
+            o_ref, l_ref = O.attend(q, k, v, pl, n_ref)
+            assert_outputs_close(g["o"], o_ref, g["lse"], l_ref)
+        elif mode == 1:
+            # a threshold in a gap of at least 2e-3 between the oracle's
+            # tile maxima (fp32 and float64 maxima cannot disagree there)
+            _, _, mx = O.exact_max_selection(q, k, pl, 0.0)
+            vals = np.sort(np.concatenate([m for m in mx.values() if len(m)]))
+            gaps = np.flatnonzero(np.diff(vals) >= 2e-3)
+            if len(gaps):
+                i = gaps[int(rng.integers(0, len(gaps)))]
+                theta = float((vals[i] + vals[i + 1]) / 2)
+            else:  # above every maximum: no sparse tile
+                theta = float(vals[-1]) + 1.0
+            say(f"[random exact] theta={theta:.4f} {tag}")
+            g = run_gpu(q, k, v, S, 0.05, max_theta=theta)
+            n_ref, masks, _ = O.exact_max_selection(q, k, pl, theta)
+            assert np.array_equal(g["n_I"], n_ref)
+            o_ref, l_ref = O.attend(q, k, v, pl, n_ref, tile_mask=masks)
+            assert_outputs_close(g["o"], o_ref, g["lse"], l_ref)
+        else:
+            K = int(rng.integers(0, 2 * N // 64))
+            say(f"[random topk] K={K} {tag}")
+            _check_topk(q, k, v, S, K)
